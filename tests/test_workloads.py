@@ -1,0 +1,103 @@
+"""The seeded input generator: determinism, slicing, shapes and distributions."""
+import json
+import os
+
+import numpy as np
+
+from workloads import (CONFIGS, Workload, bf16_bits_to_f32, make_ranks, normals,
+                       to_bf16_bits)
+
+
+def test_counter_slices_match_whole_stream():
+    whole = normals(5, 18, 3, 0, 1000)
+    for start, cnt in [(0, 1), (1, 7), (13, 100), (999, 1)]:
+        np.testing.assert_array_equal(normals(5, 18, 3, start, cnt), whole[start:start + cnt])
+    assert not np.array_equal(normals(5, 18, 4, 0, 10), whole[:10])
+    assert not np.array_equal(normals(6, 18, 3, 0, 10), whole[:10])
+
+
+def test_normals_are_standard():
+    x = normals(1, 17, 0, 0, 200_000)
+    assert abs(x.mean()) < 0.01 and abs(x.std() - 1) < 0.01
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.00390625, 1.005859375, 1.0078125, -3.14159, 0.0, 1e-30], np.float32)
+    got = bf16_bits_to_f32(to_bf16_bits(x))
+    # 1 + 2^-8 is halfway between 1 and 1 + 2^-7: ties to even -> 1
+    assert got[1] == 1.0
+    assert got[2] == np.float32(1.0078125)
+    assert got[3] == np.float32(1.0078125)
+    assert np.all(np.abs(got - x) <= np.abs(x) * 2.0 ** -8)
+
+
+def test_smaller_batch_is_prefix():
+    big = Workload(CONFIGS["c3"].with_batch(3))
+    small = Workload(CONFIGS["c3"].with_batch(2))
+    a, b = big.step(5), small.step(5)
+    for k in ("q", "k", "v", "a", "beta"):
+        np.testing.assert_array_equal(a[k][:2], b[k])
+    np.testing.assert_array_equal(big.state_batch(1), small.state_batch(1))
+
+
+def test_step_item_matches_step():
+    wl = Workload(CONFIGS["c4"].with_batch(2))
+    st = wl.step(2)
+    for (b, h) in [(0, 0), (1, 31), (1, 7)]:
+        it = wl.step_item(2, b, h)
+        for k in ("q", "k", "v", "a", "beta"):
+            np.testing.assert_array_equal(st[k][b, h], it[k])
+
+
+def test_value_distributions():
+    wl = Workload(CONFIGS["c4"].with_batch(4))
+    st = wl.step(0)
+    nk = np.linalg.norm(st["k"].astype(np.float64), axis=-1)
+    assert np.all(np.abs(nk - 1) < 5e-3)          # unit keys, up to bf16 rounding
+    assert st["a"].shape == (4, 32, 128)          # KDA: per-channel decay
+    assert np.all((st["a"] > 0) & (st["a"] < 1))
+    assert np.all((st["beta"] > 0) & (st["beta"] < 1))
+    # bf16 values: the low 16 bits of each float32 are zero
+    assert np.all(st["q"].view(np.uint32) & 0xFFFF == 0)
+    c0 = Workload(CONFIGS["c0"]).step(0)
+    assert c0["q_bits"] is None and c0["q"].dtype == np.float32
+    s = wl.state_batch(0)
+    assert abs(s.std() - 0.02) < 5e-4
+
+
+def test_basis_rows_orthonormal():
+    wl = Workload(CONFIGS["c1"].with_batch(1))
+    for g in range(wl.cfg.G):
+        om = wl.basis[g].astype(np.float64)
+        np.testing.assert_allclose(om @ om.T, np.eye(79), atol=1e-6)
+        F = wl.fmap(g, 6).astype(np.float64)
+        np.testing.assert_allclose(F @ om[:6].T, np.eye(6), atol=1e-6)
+
+
+def test_rank_tables_hit_the_budget():
+    for name, cfg in CONFIGS.items():
+        r = make_ranks(cfg)
+        assert r.shape == (cfg.H,)
+        assert (r == 0).sum() == cfg.n_dense
+        sk = r[r > 0]
+        assert sk.min() >= 1 and sk.max() <= cfg.rank_cap
+        assert sk.sum() == round(cfg.mean_rank * len(sk))
+        np.testing.assert_array_equal(r, make_ranks(cfg))
+
+
+def test_nano_layer_matches_calibration_card(golden_dir):
+    with open(os.path.join(golden_dir, "nano_card.json")) as f:
+        card = json.load(f)
+    c1 = CONFIGS["c1"]
+    assert (c1.H, c1.K, c1.V, c1.G, c1.W, c1.rank_cap) == (
+        card["state_heads_per_layer"], card["K"], card["V"], card["basis_groups_per_layer"],
+        card["window"], card["rank_cap"])
+    assert c1.basis_rows == card["basis_shape"][2] and c1.K == card["basis_shape"][3]
+    assert c1.kind == "mamba2" and card["erase_factor"] is False
+    tab = {row["mean_rank"]: row for row in card["verified_mean_ranks"]}
+    total = 27 * 128
+    assert tab[21]["dense"] + tab[21]["sketch"] == total
+    # dense fractions of the Nano-shaped workloads follow the card's table
+    assert CONFIGS["c2"].n_dense == round(tab[21]["dense"] / total * 128)
+    assert abs(tab[6]["dense"] / total - 0.01) < 0.002 and CONFIGS["c1"].n_dense == 1
+    assert abs(tab[10]["dense"] / total - 0.07) < 0.01
