@@ -1,0 +1,283 @@
+"""Per-layer decode latency and HBM bandwidth of the SketchSSM decode path.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1] [--no-cpu]
+
+A step is one decode step of one layer: the read of every (b, h) item at the
+current window position, plus the flush (apply the 16 buffered tokens, emit the
+sketch) after every 16th read.  Steps rotate over several independent layer
+instances (as a model's recurrent layers would) so that consecutive launches
+touch different memory and the 256 MB Infinity Cache cannot serve them.  All
+inputs are on the device before timing starts.
+
+Prints one JSON line.  ``value`` is microseconds per layer decode step (lower is
+better); the same line carries the achieved HBM GB/s, the read and flush kernel
+times, the full-state-read baseline, a roofline entry for the read kernel and
+the CPU oracle timed on a sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "per-layer decode µs + achieved HBM GB/s, Nano-9B layer, batch 256, mean rank 6"
+HBM_PEAK_GBPS = 8000.0
+
+
+# ---------------------------------------------------------------------------
+# algorithmic bytes (what the method has to move; no re-reads)
+# ---------------------------------------------------------------------------
+def token_bytes(cfg) -> int:
+    """One token of the window: k, v, its decay (vector for KDA) and beta."""
+    es = 2 if cfg.qkv == "bf16" else 4
+    a = 4 * cfg.K if cfg.kind == "kda" else 4
+    b = 4 if cfg.kind != "mamba2" else 0
+    return (cfg.K + cfg.V) * es + a + b
+
+
+def read_bytes(cfg, ranks, pos: int, dense_all: bool = False) -> int:
+    """Bytes of one read launch at window position pos (0-based)."""
+    es = 2 if cfg.qkv == "bf16" else 4
+    tb = token_bytes(cfg)
+    per_item_common = cfg.K * es + tb + tb + pos * tb + cfg.V * 4  # q + (k,v,a,b in) + append + window + y
+    total = 0
+    frames_rows = set()
+    for h in range(cfg.H):
+        r = 0 if dense_all else int(ranks[h])
+        state = cfg.K * cfg.V * 4 if r == 0 else r * cfg.V * 4
+        total += cfg.B * (per_item_common + state)
+    if not dense_all:
+        # each distinct coefficient map is read once per launch
+        frames_rows = {(int(h // (cfg.H // cfg.G)), int(ranks[h])) for h in range(cfg.H) if ranks[h] > 0}
+        total += sum(r for _, r in frames_rows) * cfg.K * 4
+    return total
+
+
+def flush_bytes(cfg, ranks, n_tokens: int, dense_all: bool = False) -> int:
+    total = 0
+    for h in range(cfg.H):
+        r = 0 if dense_all else int(ranks[h])
+        s = 2 * cfg.K * cfg.V * 4 if n_tokens > 0 else (cfg.K * cfg.V * 4 if r else 0)
+        total += cfg.B * (s + n_tokens * token_bytes(cfg) + r * cfg.V * 4)
+    if not dense_all:
+        total += sum(int(r) for r in ranks) * cfg.K * 4  # basis rows, once per head
+    return total
+
+
+def step_bytes(cfg, ranks, dense_all=False) -> float:
+    W = cfg.W
+    rd = np.mean([read_bytes(cfg, ranks, p, dense_all) for p in range(W)])
+    return rd + flush_bytes(cfg, ranks, W, dense_all) / W
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample
+# ---------------------------------------------------------------------------
+def cpu_baseline(cfg, wl, n_items: int = 4096):
+    from threadpoolctl import threadpool_limits
+
+    from oracle import gather_items, items_oracle
+    rng = np.random.default_rng(5)
+    H = cfg.H
+    per_head = max(1, n_items // H)
+    items = [(int(b), h) for h in range(H) for b in rng.choice(cfg.B, per_head, replace=False)]
+    steps = [wl.step(t) for t in range(cfg.W)]
+    so = [gather_items(st, items) for st in steps]
+    with threadpool_limits(limits=1):
+        orc = items_oracle(wl, items)
+        t0 = time.perf_counter()
+        for s in so:
+            orc.read(s["q"], s["k"], s["v"], s["a"], s["beta"])
+        orc.flush()
+        dt = time.perf_counter() - t0
+    us_per_step = dt / cfg.W * 1e6 * (cfg.B * cfg.H) / len(items)
+    return {"value": round(us_per_step, 1), "unit": "us per layer decode step", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{len(items)} of {cfg.B * cfg.H} (b,h) items ({per_head} random sequences per head), "
+                      f"one window of {cfg.W} reads + 1 flush, fp64 numpy, 1 thread, {dt:.1f} s; scaled to all items",
+            "host_cpus_visible": len(os.sched_getaffinity(0))}
+
+
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--config", default="c1")
+    ap.add_argument("--instances", type=int, default=4)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode path has no cross-GPU exchange and this "
+              "build runs on a single MI355X (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from rank_state_read_amd import binding as Bnd
+    from rank_state_read_amd.layer import layer_for_workload
+    from workloads import CONFIGS, Workload
+
+    def log(msg):
+        if not args.quiet:
+            print(msg, file=sys.stderr, flush=True)
+
+    cfg = CONFIGS[args.config]
+    W = cfg.W
+    NI = args.instances
+    wl = Workload(cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    lay0 = layer_for_workload(wl, device=dev)
+    log(f"state generated ({time.time() - t0:.1f}s)")
+    lays = [lay0]
+    for _ in range(NI - 1):
+        lays.append(layer_for_workload(wl, device=dev, S_init=lay0.S))
+    inputs = []
+    for t in range(W):
+        inputs.append(lay0.upload_step(wl.step(t)))
+    log(f"inputs generated ({time.time() - t0:.1f}s)")
+    dense_plan = Bnd.Plan(lay0.shape, np.zeros(cfg.H, np.int32), wl.groups)
+    for L in lays:
+        L.flush(0)
+    torch.cuda.synchronize()
+
+    def read(L, pos, y=None):
+        d = inputs[pos]
+        return L.read(pos, d["q"], d["k"], d["v"], d["a"], d["beta"], y=y)
+
+    def dense_read(L, pos):
+        d = inputs[pos]
+        return L.dense_read(pos, d["q"], d["k"], d["v"], d["a"], d["beta"])
+
+    def dense_flush(L, n):
+        Bnd.sketchssm_flush(dense_plan, L.S, None, None, L.kbuf, L.vbuf, L.abuf, L.bbuf, n)
+
+    def run_steps(n, s0, dense=False):
+        """n layer steps starting at global step s0 (instance s % NI, position (s // NI) % W)."""
+        for s in range(s0, s0 + n):
+            L = lays[s % NI]
+            pos = (s // NI) % W
+            if dense:
+                dense_read(L, pos)
+                if pos == W - 1:
+                    dense_flush(L, W)
+            else:
+                read(L, pos)
+                if pos == W - 1:
+                    L.flush(W)
+
+    def timed(fn, reps=1):
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    period = NI * W
+    K = max(period, (args.steps + period - 1) // period * period)
+    warm = max(0, args.warmup)
+    # ---- whole decode steps (the headline) -----------------------------------
+    run_steps(warm, 0)
+    torch.cuda.synchronize()
+    ms = timed(lambda: run_steps(K, warm))
+    us_step = ms * 1000.0 / K
+    log(f"sketch path: {us_step:.2f} us/step over {K} steps")
+
+    # ---- the read kernel alone, per window position ---------------------------
+    per_pos = []
+    for pos in range(W):
+        def f(pos=pos):
+            for i in range(NI):
+                read(lays[i], pos)
+        f()
+        per_pos.append(timed(f, reps=8) * 1000.0 / NI)
+    read_us = float(np.mean(per_pos))
+    # ---- the flush alone (re-applies the same window; the time is what matters) --
+    flush_us = timed(lambda: [L.flush(W) for L in lays], reps=4) * 1000.0 / NI
+    init_us = timed(lambda: [L.flush(0) for L in lays], reps=4) * 1000.0 / NI
+
+    # ---- full-state-read baseline (every head dense) ----------------------------
+    run_steps(period, 0, dense=True)
+    ms_d = timed(lambda: run_steps(K, 0, dense=True))
+    dense_step_us = ms_d * 1000.0 / K
+    dense_pos = []
+    for pos in (0, W // 2, W - 1):
+        dense_pos.append(timed(lambda pos=pos: [dense_read(L, pos) for L in lays], reps=4) * 1000.0 / NI)
+    dense_read_us = timed(lambda: [dense_read(L, p) for p in range(W) for L in lays], reps=2) * 1000.0 / (NI * W)
+    dense_flush_us = timed(lambda: [dense_flush(L, W) for L in lays], reps=4) * 1000.0 / NI
+
+    ranks = wl.ranks
+    rb = [read_bytes(cfg, ranks, p) for p in range(W)]
+    read_GBps = float(np.mean([b / (t * 1e3) for b, t in zip(rb, per_pos)]))
+    rb_avg = float(np.mean(rb))
+    fb = flush_bytes(cfg, ranks, W)
+    sb = step_bytes(cfg, ranks)
+    achieved = rb_avg / (read_us * 1e3)
+    out = {
+        "metric": METRIC,
+        "value": round(us_step, 3),
+        "unit": "us per layer decode step",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": warm,
+        "ms_per_step": round(us_step / 1000.0, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "hbm_GBps": round(sb / (us_step * 1e3), 1),
+        "config": {"workload": f"{cfg.name}: Nemotron-Nano-9B-v2-shaped Mamba-2 layer, B={cfg.B} H={cfg.H} "
+                               f"K={cfg.K} V={cfg.V} W={W}, mean rank {cfg.mean_rank}, "
+                               f"{int((ranks == 0).sum())} dense head(s), bf16 q/k/v, fp32 state",
+                   "global_batch": cfg.B, "layer_instances": NI, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "read_kernel (sketchssm_decode_read)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "bytes_per_launch": int(rb_avg), "avg_launch_us": round(read_us, 3)},
+        "detail": {
+            "read_us_mean": round(read_us, 3),
+            "read_us_per_pos": [round(x, 2) for x in per_pos],
+            "read_GBps": round(read_GBps, 1),
+            "flush_us": round(flush_us, 2),
+            "flush_GBps": round(fb / (flush_us * 1e3), 1),
+            "initial_sketch_us": round(init_us, 2),
+            "layer_us_model": round(read_us + flush_us / W, 3),
+            "step_bytes": int(sb),
+            "dense_step_us": round(dense_step_us, 3),
+            "dense_read_us_mean": round(dense_read_us, 3),
+            "dense_read_us_pos0_mid_last": [round(x, 2) for x in dense_pos],
+            "dense_read_GBps": round(np.mean([read_bytes(cfg, ranks, p, True) for p in range(W)])
+                                     / (dense_read_us * 1e3), 1),
+            "dense_flush_us": round(dense_flush_us, 2),
+            "read_ratio_dense_over_sketch": round(dense_read_us / read_us, 3),
+            "layer_ratio_dense_over_sketch": round(dense_step_us / us_step, 3),
+        },
+    }
+    if not args.no_cpu:
+        log("timing the CPU oracle on a sample ...")
+        out["cpu_baseline"] = cpu_baseline(cfg, wl)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,19 @@
+"""SketchSSM decode hot path for MI355X (gfx950): Python binding of libsketchssm.so.
+
+The HIP library does all the work; this package only loads it and marshals
+arguments.  Import fails loudly at first use if the library is not built.
+"""
+from .binding import (  # noqa: F401
+    DTYPE,
+    KIND,
+    LIB_PATH,
+    Plan,
+    Shape,
+    SketchSSMError,
+    lib,
+    make_shape,
+    sketchssm_decode_read,
+    sketchssm_dense_read,
+    sketchssm_flush,
+    status_string,
+)

@@ -1,0 +1,136 @@
+"""Caller-side device buffers of one recurrent layer, allocated with torch.
+
+The library allocates nothing; this helper owns the state cache, the sketch,
+the window, the packed frames and the output of one layer and forwards to the
+C entry points.  It does no arithmetic of the decode path: it only allocates,
+copies inputs in and lays out the frames array in the plan's frame order.
+"""
+from __future__ import annotations
+
+from typing import Callable, Optional
+
+import numpy as np
+import torch
+
+from . import binding as _b
+
+
+def _to_device(x, dtype, device):
+    if isinstance(x, torch.Tensor):
+        return x.to(device=device, dtype=dtype).contiguous()
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device=device, dtype=dtype).contiguous()
+
+
+def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
+    """A bfloat16 device tensor holding the given raw 16-bit patterns."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+class SketchLayer:
+    """One layer's buffers for ``sketchssm_flush`` / ``sketchssm_decode_read``.
+
+    rank, group : int32 [H] (rank 0 = dense fallback)
+    basis       : float32 [G, basis_rows, K]
+    fmap        : callable (group, rank) -> float32 [rank, K] coefficient map
+    S_init      : float32 [B, H, K, V] (numpy or tensor), or None to leave S empty
+    """
+
+    def __init__(self, *, B: int, H: int, K: int, V: int, W: int, G: int, basis_rows: int,
+                 rank_cap: int, kind: str, qkv: str, rank, group, basis,
+                 fmap: Optional[Callable] = None, S_init=None, device="cuda"):
+        self.kind, self.qkv = kind, qkv
+        self.B, self.H, self.K, self.V, self.W = B, H, K, V, W
+        self.device = torch.device(device)
+        self.shape = _shape(B, H, K, V, W, G, basis_rows, rank_cap, kind, qkv)
+        self.plan = _plan(self.shape, rank, group)
+        self.layout = self.plan.export()
+        dev = self.device
+        self.S = torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
+        if S_init is not None:
+            self.S.copy_(_to_device(S_init, torch.float32, dev))
+        nz = self.plan.z_elems
+        self.Z = torch.zeros(max(nz, 4), dtype=torch.float32, device=dev) if nz else None
+        self.basis = _to_device(basis, torch.float32, dev)
+        nf = self.plan.frame_elems
+        self.frames = None
+        if nf:
+            packed = np.zeros(nf, dtype=np.float32)
+            off = self.layout["frame_row_off"]
+            for f, (g, r) in enumerate(self.layout["frames"]):
+                packed[off[f] * K:(off[f] + r) * K] = np.asarray(fmap(g, r), np.float32).reshape(-1)
+            self.frames = _to_device(packed, torch.float32, dev)
+        qdt = torch.bfloat16 if qkv == "bf16" else torch.float32
+        self.qdtype = qdt
+        self.kbuf = torch.zeros((B, H, W, K), dtype=qdt, device=dev)
+        self.vbuf = torch.zeros((B, H, W, V), dtype=qdt, device=dev)
+        self.abuf = torch.zeros((B, H, W, K) if kind == "kda" else (B, H, W), dtype=torch.float32, device=dev)
+        self.bbuf = torch.zeros((B, H, W), dtype=torch.float32, device=dev) if kind != "mamba2" else None
+        self.y = torch.empty((B, H, V), dtype=torch.float32, device=dev)
+
+    # -- inputs ------------------------------------------------------------
+    def upload_step(self, st: dict) -> dict:
+        """Copy one step's inputs (the ``workloads`` dict layout) to the device."""
+        dev = self.device
+        out = {}
+        for key in ("q", "k", "v"):
+            if self.qkv == "bf16":
+                out[key] = bf16_tensor(st[key + "_bits"], dev)
+            else:
+                out[key] = _to_device(st[key], torch.float32, dev)
+        out["a"] = _to_device(st["a"], torch.float32, dev)
+        out["beta"] = None if st.get("beta") is None else _to_device(st["beta"], torch.float32, dev)
+        return out
+
+    # -- the entry points -----------------------------------------------------
+    def flush(self, n_tokens: int, stream=None):
+        _b.sketchssm_flush(self.plan, self.S, self.Z, self.basis, self.kbuf, self.vbuf, self.abuf,
+                          self.bbuf, n_tokens, stream)
+
+    def read(self, pos: int, q, k, v, a, beta=None, y=None, stream=None) -> torch.Tensor:
+        y = self.y if y is None else y
+        _b.sketchssm_decode_read(self.plan, self.S, self.Z, self.frames, q, k, v, a, beta, self.kbuf,
+                                self.vbuf, self.abuf, self.bbuf, pos, y, stream)
+        return y
+
+    def dense_read(self, pos: int, q, k, v, a, beta=None, y=None, stream=None) -> torch.Tensor:
+        y = self.y if y is None else y
+        _b.sketchssm_dense_read(self.shape, self.S, q, k, v, a, beta, self.kbuf, self.vbuf, self.abuf,
+                               self.bbuf, pos, y, stream)
+        return y
+
+    # -- views ---------------------------------------------------------------
+    def z_item(self, b: int, h: int) -> Optional[torch.Tensor]:
+        """The (rank x V) sketch rows of item (b, h), or None for a dense head."""
+        r = int(self.plan.rank[h])
+        if r == 0:
+            return None
+        z0 = int(self.layout["z_row_off"][h])
+        start = (z0 * self.B + b * r) * self.V
+        return self.Z[start:start + r * self.V].view(r, self.V)
+
+    def z_items(self, items) -> list:
+        return [self.z_item(b, h) for (b, h) in items]
+
+
+def _shape(B_, H, K, V, W, G, basis_rows, rank_cap, kind, qkv):
+    return _b.make_shape(B_, H, K, V, W, G, basis_rows, rank_cap, kind, qkv)
+
+
+def _plan(shape, rank, group):
+    return _b.Plan(shape, rank, group)
+
+
+def layer_for_workload(wl, *, ranks=None, device="cuda", S_init=None, with_state=True) -> SketchLayer:
+    """A SketchLayer for a ``workloads.Workload`` (ranks may be overridden, e.g. all zero)."""
+    c = wl.cfg
+    rk = wl.ranks if ranks is None else np.asarray(ranks, np.int32)
+    lay = SketchLayer(B=c.B, H=c.H, K=c.K, V=c.V, W=c.W, G=c.G, basis_rows=c.basis_rows,
+                      rank_cap=c.rank_cap, kind=c.kind, qkv=c.qkv, rank=rk, group=wl.groups,
+                      basis=wl.basis, fmap=wl.fmap, S_init=None, device=device)
+    if S_init is not None:
+        lay.S.copy_(_to_device(S_init, torch.float32, lay.device))
+    elif with_state:
+        for b in range(c.B):
+            lay.S[b].copy_(torch.from_numpy(wl.state_batch(b)))
+    return lay

@@ -1,0 +1,157 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol, its
+planner matches the oracle's plan rule bit for bit, and argument errors come
+back as status codes before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import plan as oracle_plan
+from rank_state_read_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "sketchssm.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sketchssm_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    syms = _declared_symbols()
+    assert len(syms) >= 9
+    L = B.lib()
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(syms) == set(B._PROTOS)
+
+
+def _shape(H=8, G=2, B_=4, V=80, kind="mamba2", qkv="bf16", cap=49, rows=79):
+    return B.make_shape(B_, H, 128, V, 16, G, rows, cap, kind, qkv)
+
+
+def test_plan_matches_oracle_rule_bit_exact():
+    rng = np.random.default_rng(11)
+    for trial in range(300):
+        H = int(rng.integers(1, 257))
+        G = int(rng.integers(1, 9))
+        cap = int(rng.integers(1, 65))
+        rows = int(rng.integers(1, 80))
+        rmax = min(cap, rows, 128)
+        rank = rng.integers(0, rmax + 1, size=H).astype(np.int32)
+        rank[rng.random(H) < rng.random()] = 0
+        group = rng.integers(0, G, size=H).astype(np.int32)
+        p = B.Plan(_shape(H=H, G=G, cap=cap, rows=rows), rank, group)
+        got = p.export()
+        want = oracle_plan(rank, group, G, 128, rows, cap)
+        assert got["frames"] == [tuple(f) for f in want["frames"]]
+        for key in ("frame_index", "frame_row_off", "z_row_off", "bucket", "order"):
+            assert np.array_equal(got[key], want[key]), (trial, key)
+        assert p.z_elems == 4 * 80 * int(rank.sum())
+        assert p.frame_elems == 128 * sum(r for _, r in want["frames"])
+
+
+def test_plan_hand_example_from_library(golden_dir):
+    import json
+    with open(os.path.join(golden_dir, "plan_small.json")) as f:
+        g = json.load(f)
+    p = B.Plan(_shape(H=8, G=g["G"]), np.array(g["rank"]), np.array(g["group"]))
+    got = p.export()
+    assert [list(x) for x in got["frames"]] == g["frames"]
+    for key in ("frame_index", "frame_row_off", "z_row_off", "bucket", "order"):
+        assert got[key].tolist() == g[key], key
+
+
+@pytest.mark.parametrize("bad", [
+    dict(H=0), dict(H=257), dict(V=96), dict(G=0), dict(cap=65), dict(B_=0),
+])
+def test_plan_rejects_bad_shapes(bad):
+    kw = dict(H=8, G=2)
+    kw.update(bad)
+    H = max(kw["H"], 1)
+    with pytest.raises(B.SketchSSMError) as e:
+        B.Plan(_shape(**kw), np.ones(H, np.int32), np.zeros(H, np.int32))
+    assert e.value.status == 2
+
+
+def test_plan_rejects_bad_tables():
+    for rank, group in [([50] + [1] * 7, [0] * 8), ([-1] + [1] * 7, [0] * 8),
+                        ([1] * 8, [2] + [0] * 7), ([80] + [1] * 7, [0] * 8)]:
+        with pytest.raises(B.SketchSSMError) as e:
+            B.Plan(_shape(), np.array(rank), np.array(group))
+        assert e.value.status == 2
+    # rank above basis_rows
+    with pytest.raises(B.SketchSSMError):
+        B.Plan(_shape(rows=5), np.array([6] + [1] * 7), np.zeros(8))
+
+
+def test_bad_kind_and_dtype():
+    for kw in (dict(kind=3), dict(qkv=2)):
+        with pytest.raises(B.SketchSSMError) as e:
+            B.Plan(_shape(**kw), np.ones(8, np.int32), np.zeros(8, np.int32))
+        assert e.value.status == 1
+
+
+# Host-side argument checks of the launch entry points: every case below is
+# rejected before any HIP call, so no device is touched.
+FAKE = 1 << 20  # a 16-byte-aligned stand-in address, never dereferenced
+
+
+def test_read_argument_errors():
+    p = B.Plan(_shape(), np.array([0, 1, 2, 3, 4, 5, 6, 7]), np.zeros(8, np.int32))
+    L = B.lib()
+    args = dict(S=FAKE, Z=FAKE, frames=FAKE, q=FAKE, k=FAKE, v=FAKE, a=FAKE, beta=None,
+                kbuf=FAKE, vbuf=FAKE, abuf=FAKE, bbuf=None, pos=0, y=FAKE)
+
+    def call(**over):
+        a = dict(args)
+        a.update(over)
+        return L.sketchssm_decode_read(p.handle, a["S"], a["Z"], a["frames"], a["q"], a["k"], a["v"],
+                                       a["a"], a["beta"], a["kbuf"], a["vbuf"], a["abuf"], a["bbuf"],
+                                       a["pos"], a["y"], None)
+
+    assert call(pos=-1) == 1
+    assert call(pos=16) == 1
+    assert call(q=None) == 1
+    assert call(y=None) == 1
+    assert call(S=None) == 1          # a dense head is present
+    assert call(Z=None) == 1          # sketch heads are present
+    assert call(beta=FAKE) == 1       # Mamba-2 takes no beta
+    assert call(q=FAKE + 4) == 3      # misaligned
+    assert L.sketchssm_decode_read(None, *([None] * 12), 0, None, None) == 1
+
+
+def test_flush_argument_errors():
+    sh = _shape(kind="gdn", V=128)
+    p = B.Plan(sh, np.array([0, 1, 2, 3, 4, 5, 6, 7]), np.zeros(8, np.int32))
+    L = B.lib()
+
+    def call(S=FAKE, Z=FAKE, basis=FAKE, kb=FAKE, vb=FAKE, ab=FAKE, bb=FAKE, n=16):
+        return L.sketchssm_flush(p.handle, S, Z, basis, kb, vb, ab, bb, n, None)
+
+    assert call(n=-1) == 1
+    assert call(n=17) == 1
+    assert call(S=None) == 1
+    assert call(Z=None) == 1
+    assert call(bb=None) == 1         # delta rule needs beta
+    assert call(basis=FAKE + 8) == 3
+
+
+def test_dense_read_argument_errors():
+    L = B.lib()
+    bad = _shape(V=96)
+    assert L.sketchssm_dense_read(ctypes.byref(bad), *([FAKE] * 5), None, FAKE, FAKE, FAKE, None, 0,
+                                  FAKE, None) == 2
+    ok = _shape()
+    assert L.sketchssm_dense_read(ctypes.byref(ok), *([FAKE] * 5), None, FAKE, FAKE, FAKE, None, 99,
+                                  FAKE, None) == 1
+
+
+def test_status_strings():
+    for s in range(7):
+        assert B.status_string(s)
+    assert "unknown" in B.status_string(42)

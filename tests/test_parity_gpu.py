@@ -1,0 +1,315 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Every decode step's y, and S and Z after every flush, are compared with the
+float64 oracle on the same seeded inputs.  The bar is a relative error of 1e-4
+per slab, max |gpu - ref| / max |ref|, where a slab is one (t, b, h) output
+vector, one item's K x V state or one item's r x V sketch; integer tables are
+compared bit for bit in the CPU tests.
+"""
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+from oracle import gather_items, items_oracle  # noqa: E402
+from workloads import CONFIGS, Config, Workload  # noqa: E402
+
+TOL = 1e-4
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from rank_state_read_amd import binding
+    binding.lib()
+
+
+def _slab_err(got, ref):
+    """max over slabs of max|got-ref| / max|ref|; slabs along the leading axis."""
+    got = np.asarray(got, np.float64).reshape(len(ref), -1)
+    ref = np.asarray(ref, np.float64).reshape(len(ref), -1)
+    den = np.maximum(np.abs(ref).max(axis=1), 1e-30)
+    return float((np.abs(got - ref).max(axis=1) / den).max())
+
+
+class Run:
+    """Drive one layer on the GPU and the oracle on a set of (b, h) items."""
+
+    def __init__(self, wl, items=None, dense_baseline=False, step_source=None):
+        from rank_state_read_amd.layer import layer_for_workload
+        self.wl = wl
+        c = wl.cfg
+        self.cfg = c
+        self.dense = dense_baseline
+        self.src = step_source or wl
+        self.lay = layer_for_workload(wl)
+        self.items = items if items is not None else [(b, h) for b in range(c.B) for h in range(c.H)]
+        S0 = np.stack([self.lay.S[b, h].cpu().numpy() for (b, h) in self.items]) \
+            if len(self.items) < c.B * c.H else self.lay.S.cpu().numpy().reshape(-1, c.K, c.V)
+        self.orc = items_oracle(wl, self.items, S_init=S0)
+        self.bi = np.array([b for b, _ in self.items])
+        self.hi = np.array([h for _, h in self.items])
+        self.sketch_items = [i for i, (b, h) in enumerate(self.items) if wl.ranks[h] > 0]
+        self.t = 0
+        self.max_err = {"y": 0.0, "S": 0.0, "Z": 0.0}
+
+    def init_sketch(self):
+        self.lay.flush(0)
+        torch.cuda.synchronize()
+        self.check_Z()
+
+    def check_S(self):
+        S = self.lay.S[torch.as_tensor(self.bi), torch.as_tensor(self.hi)].cpu().numpy()
+        e = _slab_err(S, self.orc.S0)
+        self.max_err["S"] = max(self.max_err["S"], e)
+        assert e <= TOL, f"S after flush at t={self.t}: {e:.3e}"
+
+    def check_Z(self):
+        if not self.sketch_items:
+            return
+        got = []
+        ref = []
+        for i in self.sketch_items:
+            b, h = self.items[i]
+            r = int(self.wl.ranks[h])
+            got.append(self.lay.z_item(b, h).cpu().numpy())
+            ref.append(self.orc.Z[i, :r])
+        e = max(_slab_err(g[None], rr[None]) for g, rr in zip(got, ref))
+        self.max_err["Z"] = max(self.max_err["Z"], e)
+        assert e <= TOL, f"Z at t={self.t}: {e:.3e}"
+
+    def step(self, check=True):
+        c = self.cfg
+        st = self.src.step(self.t)
+        dev = self.lay.upload_step(st)
+        pos = self.t % c.W
+        if self.dense:
+            y = self.lay.dense_read(pos, dev["q"], dev["k"], dev["v"], dev["a"], dev["beta"])
+        else:
+            y = self.lay.read(pos, dev["q"], dev["k"], dev["v"], dev["a"], dev["beta"])
+        if pos == c.W - 1:
+            self.lay.flush(c.W)
+        so = gather_items(st, self.items)
+        yo, _ = self.orc.read(so["q"], so["k"], so["v"], so["a"], so["beta"])
+        torch.cuda.synchronize()
+        self.t += 1
+        if check:
+            yg = y[torch.as_tensor(self.bi), torch.as_tensor(self.hi)].cpu().numpy()
+            e = _slab_err(yg, yo)
+            self.max_err["y"] = max(self.max_err["y"], e)
+            assert e <= TOL, f"y at t={self.t - 1} (pos {pos}): {e:.3e}"
+        if self.orc.j == c.W:
+            self.orc.flush()
+            if check:
+                self.check_S()
+                self.check_Z()
+
+
+def _run_steps(wl, steps, **kw):
+    r = Run(wl, **kw)
+    r.init_sketch()
+    t0 = time.time()
+    for _ in range(steps):
+        r.step()
+    _log(f"  {wl.cfg.name} B={wl.cfg.B} steps={steps} max errors {r.max_err} ({time.time() - t0:.1f}s)")
+    return r
+
+
+# ---------------------------------------------------------------------------
+# every output of reduced batches (two full tiles of 16 rows and a ragged tail)
+# ---------------------------------------------------------------------------
+@pytest.mark.timeout(300)
+def test_c0_all_steps():
+    _run_steps(Workload(CONFIGS["c0"]), CONFIGS["c0"].steps)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,B,steps", [("c1", 20, 48), ("c2", 20, 40), ("c3", 37, 48),
+                                          ("c4", 37, 48)])
+def test_reduced_batch_all_items(name, B, steps):
+    _run_steps(Workload(CONFIGS[name].with_batch(B)), steps)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", ["c1", "c3", "c4"])
+def test_long_run_drift(name):
+    """Many windows on a few items: errors must not grow with the flush count."""
+    cfg = CONFIGS[name].with_batch(3)
+    wl = Workload(cfg)
+    hs = [int(np.argmax(wl.ranks)), int(np.argmin(wl.ranks)), 0]
+    items = [(b, h) for b in range(3) for h in hs]
+    _run_steps(wl, 12 * cfg.W, items=items)
+
+
+# ---------------------------------------------------------------------------
+# full sizes, in the launch configuration the benchmark times, sampled items
+# ---------------------------------------------------------------------------
+def _sample_items(wl):
+    c = wl.cfg
+    items = []
+    seen = set()
+    for h in range(c.H):
+        r = int(wl.ranks[h])
+        key = ("d", h) if r == 0 else (int(wl.groups[h]), r)
+        if key in seen:
+            continue
+        seen.add(key)
+        for b in (0, c.B - 1):
+            items.append((b, h))
+    rng = np.random.default_rng(c.seed)
+    for _ in range(16):
+        items.append((int(rng.integers(c.B)), int(rng.integers(c.H))))
+    return sorted(set(items))
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_full_size_sampled(name):
+    cfg = CONFIGS[name].with_steps(CONFIGS[name].W + 4)
+    wl = Workload(cfg)
+    items = _sample_items(wl)
+    _log(f"  {name}: full size B={cfg.B}, {len(items)} sampled items")
+    _run_steps(wl, cfg.steps, items=items)
+
+
+# ---------------------------------------------------------------------------
+# the dense-read baseline
+# ---------------------------------------------------------------------------
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,B", [("c1", 20), ("c3", 19), ("c4", 19), ("c0", 2)])
+def test_dense_read_baseline(name, B):
+    cfg = CONFIGS[name].with_batch(B)
+    wl = Workload(cfg)
+    wl0 = Workload(cfg, ranks=np.zeros(cfg.H, np.int32), basis=wl.basis)
+    _run_steps(wl0, 2 * cfg.W + 3, dense_baseline=True, step_source=wl)
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+def _edge_cfg(kind, V, B=19, cap=49):
+    return Config(f"edge-{kind}-{V}", kind, B=B, H=8, K=128, V=V, G=2, W=16, steps=40,
+                  qkv="bf16", mean_rank=6, rank_cap=cap, n_dense=0, seed=77)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("kind,V", [("mamba2", 80), ("mamba2", 64), ("gdn", 128), ("kda", 128),
+                                    ("kda", 80)])
+def test_rank_extremes(kind, V):
+    """Ranks at 1, at tile edges (16, 17, 32, 33), at the cap, mixed with dense heads."""
+    cfg = _edge_cfg(kind, V, cap=64)
+    ranks = np.array([1, 16, 0, 17, 64, 33, 49, 0], np.int32)
+    _run_steps(Workload(cfg, ranks=ranks), 2 * cfg.W + 5)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("kind,V", [("mamba2", 80), ("gdn", 128), ("kda", 128)])
+def test_single_sequence_all_dense_and_all_sketch(kind, V):
+    cfg = _edge_cfg(kind, V, B=1)
+    _run_steps(Workload(cfg, ranks=np.zeros(8, np.int32)), cfg.W + 3)
+    _run_steps(Workload(cfg, ranks=np.array([3, 5, 7, 9, 11, 13, 15, 49], np.int32)), cfg.W + 3)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("kind,V", [("mamba2", 80), ("gdn", 128), ("kda", 128)])
+def test_flush_without_tokens_keeps_state_bitwise(kind, V):
+    cfg = _edge_cfg(kind, V)
+    wl = Workload(cfg)
+    r = Run(wl)
+    before = r.lay.S.clone()
+    r.init_sketch()                     # flush(n_tokens = 0): Z only
+    assert torch.equal(before, r.lay.S)
+    for _ in range(5):
+        r.step()
+    before = r.lay.S.clone()
+    r.lay.flush(0)
+    torch.cuda.synchronize()
+    assert torch.equal(before, r.lay.S)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("kind,V", [("mamba2", 80), ("gdn", 128), ("kda", 128)])
+def test_partial_window_flush(kind, V):
+    """Flush after 5 tokens, then keep decoding from window slot 0."""
+    cfg = _edge_cfg(kind, V)
+    wl = Workload(cfg)
+    r = Run(wl)
+    r.init_sketch()
+    for _ in range(5):
+        r.step()
+    r.lay.flush(5)
+    r.orc.flush()
+    torch.cuda.synchronize()
+    r.check_S()
+    r.check_Z()
+    # continue: the next window starts at slot 0
+    base = r.t
+    for _ in range(cfg.W + 2):
+        c = cfg
+        st = wl.step(r.t)
+        dev = r.lay.upload_step(st)
+        pos = (r.t - base) % c.W
+        y = r.lay.read(pos, dev["q"], dev["k"], dev["v"], dev["a"], dev["beta"])
+        if pos == c.W - 1:
+            r.lay.flush(c.W)
+        so = gather_items(st, r.items)
+        yo, _ = r.orc.read(so["q"], so["k"], so["v"], so["a"], so["beta"])
+        torch.cuda.synchronize()
+        yg = y[torch.as_tensor(r.bi), torch.as_tensor(r.hi)].cpu().numpy()
+        assert _slab_err(yg, yo) <= TOL
+        r.t += 1
+        if r.orc.j == c.W:
+            r.orc.flush()
+            r.check_S()
+            r.check_Z()
+
+
+@pytest.mark.timeout(300)
+def test_bitwise_reproducible():
+    cfg = CONFIGS["c4"].with_batch(5)
+    outs = []
+    for _ in range(2):
+        from rank_state_read_amd.layer import layer_for_workload
+        wl = Workload(cfg)
+        lay = layer_for_workload(wl)
+        lay.flush(0)
+        ys = []
+        for t in range(cfg.W + 2):
+            dev = lay.upload_step(wl.step(t))
+            ys.append(lay.read(t % cfg.W, dev["q"], dev["k"], dev["v"], dev["a"], dev["beta"]).clone())
+            if t % cfg.W == cfg.W - 1:
+                lay.flush(cfg.W)
+        torch.cuda.synchronize()
+        outs.append((torch.stack(ys), lay.S.clone(), lay.Z.clone()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.timeout(120)
+def test_sketch_heads_do_not_read_the_state():
+    """Sketch heads' outputs do not depend on S between flushes (only dense heads read it)."""
+    from rank_state_read_amd.layer import layer_for_workload
+    cfg = CONFIGS["c1"].with_batch(4)
+    wl = Workload(cfg)
+    lay = layer_for_workload(wl)
+    lay.flush(0)
+    dev = lay.upload_step(wl.step(0))
+    y1 = lay.read(0, dev["q"], dev["k"], dev["v"], dev["a"], dev["beta"]).clone()
+    lay.S.fill_(float("nan"))
+    y2 = lay.read(0, dev["q"], dev["k"], dev["v"], dev["a"], dev["beta"]).clone()
+    torch.cuda.synchronize()
+    sk = torch.as_tensor(wl.ranks > 0)
+    assert torch.equal(y1[:, sk], y2[:, sk])
+    assert torch.isnan(y2[:, ~sk]).all()
