@@ -130,10 +130,13 @@ size_t sketchssm_frame_elems(const sketchssm_plan* plan);
  *          unchanged and only writes Z (the initial sketch after prefill).
  *   Z      device [sketchssm_z_elems] fp32, out; may be NULL when no head has a rank
  *   basis  device [G, basis_rows, K] fp32
- *   kbuf   device [B,H,W,K] of the qkv dtype      (window keys)
- *   vbuf   device [B,H,W,V] of the qkv dtype      (window values)
- *   abuf   device [B,H,W] fp32 (Mamba-2, GDN) or [B,H,W,K] fp32 (KDA) (decays)
- *   bbuf   device [B,H,W] fp32 (GDN, KDA); must be NULL for Mamba-2
+ *   kbuf   device [W,H,B,K] of the qkv dtype      (window keys)
+ *   vbuf   device [W,H,B,V] of the qkv dtype      (window values)
+ *   abuf   device [W,H,B] fp32 (Mamba-2, GDN) or [W,H,B,K] fp32 (KDA) (decays)
+ *   bbuf   device [W,H,B] fp32 (GDN, KDA); must be NULL for Mamba-2
+ *          The window is slot-major: slot i of item (b, h) is element
+ *          (i*H + h)*B + b.  A decode step then appends one contiguous slab and
+ *          reads older slots as contiguous runs of batch rows.
  *   n_tokens 0 .. W
  * The window is not modified; the next window simply starts again at slot 0.
  */

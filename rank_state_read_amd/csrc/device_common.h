@@ -124,6 +124,22 @@ __device__ __forceinline__ float dot8(const float* a, const float* b) {
     return s0 + s1;
 }
 
+// Raw buffer access: one 32-bit per-lane byte offset plus a wave-uniform byte
+// offset, so rows far apart cost no per-lane 64-bit address arithmetic.  The
+// resource covers `bytes` from `base`; accesses beyond it read 0 / are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, int(bytes),
+                                             0x00020000 /* 32-bit data format */);
+}
+
+__device__ __forceinline__ float buffer_load_f32(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ void buffer_store_f32(float x, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, x), r, voff, soff, 0);
+}
+
 // D(16x16) += A(16x4) B(4x16), fp32 in and out.  Operand lanes: A[i][kk] in
 // lane i + 16 kk, B[kk][j] in lane j + 16 kk; D[i][j] in lane j + 16 (i / 4),
 // register i % 4.

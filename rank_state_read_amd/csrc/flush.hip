@@ -1,10 +1,11 @@
 // SketchSSM flush + sketch for gfx950.
 //
-// One block per (b, h) item, consecutive blocks on the same head.  The block
-// has V/16 waves; wave w owns value columns 16w .. 16w+15 of the item's fp32
-// state and holds all K = 128 key rows of them in registers as eight 16x16
-// MFMA accumulator tiles (lane l, register r <-> S[16 kt + 4 (l/16) + r]
-// [16 w + l%16]).  In one pass over the state it
+// One block per (b, h) item; consecutive blocks walk the batch of one head, so
+// the head's basis rows stay in L2.  The block has V/16 waves; wave w owns
+// value columns 16w .. 16w+15 of the item's fp32 state and holds all K = 128
+// key rows of them in registers as eight 16x16 MFMA accumulator tiles
+// (lane l, register r <-> S[16 kt + 4 (l/16) + r][16 w + l%16]).  In one pass
+// over the state it
 //   1. applies the window's n buffered tokens (page "SketchSSM: Write to the
 //      Full State, Read from a Compact Sketch", Abstract: buffered keys and
 //      values, periodic exact state updates; W = 16 on the Nemotron Nano 9B v2
@@ -24,6 +25,11 @@
 // The state tiles serve directly as the B operand of G and Z: the register
 // index r of a tile is used as the 4-wide K step, which only permutes the
 // order of the key sum, and the A operand is read with the same permutation.
+//
+// Latency: the small loads (window, decays, basis rows) are issued before the
+// 40-64 KB state load, so staging them never waits behind the state; scalar
+// decay products are formed per thread from the 16 decays, so Mamba-2 needs a
+// single barrier per item.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -59,12 +65,11 @@ struct FlushLds {
     static constexpr int US = VStride<V>::value;
     static constexpr int kt = 0;                                  // [16][kKtStride]
     static constexpr int u = kt + 16 * kKtStride;                 // [16][US]
-    static constexpr int nd = kda ? 16 * kK : 16;                 // decay arrays
-    static constexpr int alpha = u + 16 * US;                     // a_i (per channel for KDA)
+    static constexpr int nd = kda ? 16 * kK : 0;                  // KDA decay arrays
+    static constexpr int alpha = u + 16 * US;
     static constexpr int gam = alpha + nd;
     static constexpr int sig = gam + nd;
-    static constexpr int beta = sig + nd;                         // [16]
-    static constexpr int kr = beta + 16;                          // delta: raw k [16][K]
+    static constexpr int kr = sig + nd;                           // delta: raw k [16][K]
     static constexpr int kg = kr + (delta ? 16 * kK : 0);         // delta: [K][kKgStride]
     static constexpr int lm = kg + (delta ? kK * kKgStride : 0);  // delta: L [16][16]
     static constexpr int om = lm + (delta ? 256 : 0);             // Omega^T [K][16 omt + 4]
@@ -82,6 +87,10 @@ __global__ __launch_bounds__(V / 16 * 64) void flush_kernel(FlushArgs A, HeadTab
     constexpr bool DELTA = L::delta;
     constexpr bool KDA = L::kda;
     constexpr int US = L::US;
+    constexpr int KCH = W * K / 8;  // 8-element key chunks of the window
+    constexpr int VCH = W * V / 8;  // 8-element value chunks
+    constexpr int ACH = W * K / 4;  // float4 chunks of KDA decays
+    constexpr int NA = (ACH + NT - 1) / NT;
     extern __shared__ float4 lds4[];
     float* sm = reinterpret_cast<float*>(lds4);
     float* Kt = sm + L::kt;
@@ -89,7 +98,6 @@ __global__ __launch_bounds__(V / 16 * 64) void flush_kernel(FlushArgs A, HeadTab
     float* al = sm + L::alpha;
     float* gam = sm + L::gam;
     float* sig = sm + L::sig;
-    float* bet = sm + L::beta;
     float* Kr = sm + L::kr;
     float* KgT = sm + L::kg;
     float* Lm = sm + L::lm;
@@ -108,41 +116,71 @@ __global__ __launch_bounds__(V / 16 * 64) void flush_kernel(FlushArgs A, HeadTab
     const size_t item = size_t(b) * A.H + h;
     const int n = A.n_tokens;
     const bool sketch = r > 0 && A.Z != nullptr;
-    const int omt = A.omt;
-    const int oms = 16 * omt + 4;
+    const int oms = 16 * A.omt + 4;
     const int v0 = 16 * w;
+    // window slot i of this item: [W][H][B] layout, slot-major
+    auto wslot = [&](int i) { return (size_t(i) * A.H + h) * A.B + b; };
 
-    // 0. issue the state loads (this wave's 16 columns, all key rows)
-    float* Si = A.S + item * size_t(K) * V;
+    // ---- 1. small loads first: window chunk, decays, betas ----
+    typename V8::raw_t kraw = V8::zero(), vraw = V8::zero();
+    const int ki = tid >> 4, kk0 = (tid & 15) * 8;            // key chunk of this thread
+    const int vi = tid / (V / 8), vc0 = (tid % (V / 8)) * 8;  // value chunk of this thread
+    float4 a4[KDA ? NA : 1];
+    float as[W], bs[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+        as[i] = 1.f;
+        bs[i] = 0.f;
+    }
+    if (n > 0) {
+        if (tid < KCH && ki < n) kraw = V8::load(A.kbuf, wslot(ki) * K + kk0);
+        if (tid < VCH && vi < n) vraw = V8::load(A.vbuf, wslot(vi) * V + vc0);
+        if (KDA) {
+#pragma unroll
+            for (int j = 0; j < NA; ++j) {
+                const int c = tid + j * NT;
+                a4[j] = make_float4(1.f, 1.f, 1.f, 1.f);
+                if (c < ACH && (c >> 5) < n)
+                    a4[j] = *reinterpret_cast<const float4*>(A.abuf + wslot(c >> 5) * K + (c & 31) * 4);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < W; ++i) as[i] = i < n ? A.abuf[wslot(i)] : 1.f;
+        }
+        if (DELTA) {
+#pragma unroll
+            for (int i = 0; i < W; ++i) bs[i] = i < n ? A.bbuf[wslot(i)] : 0.f;
+        }
+    }
+
+    // ---- 2. the state: this wave's 16 columns, all key rows ----
+    const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(A.S + item * size_t(K) * V, K * V * 4);
+    const int svo = (4 * lq * V + v0 + lr) * 4;  // this lane's byte offset in a 16-row tile
     f32x4 s[8];
 #pragma unroll
     for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) s[kt][rr] = Si[(16 * kt + 4 * lq + rr) * V + v0 + lr];
+        for (int rr = 0; rr < 4; ++rr) s[kt][rr] = buffer_load_f32(srs, svo, (16 * kt + rr) * V * 4);
 
-    // 1. decays, betas and the basis rows
-    if (n > 0) {
-        const size_t wbase = item * W;
-        if (KDA) {
-            for (int e = tid; e < W * K; e += NT) al[e] = (e / K < n) ? A.abuf[wbase * K + e] : 1.f;
-        } else if (tid < W) {
-            al[tid] = tid < n ? A.abuf[wbase + tid] : 1.f;
-        }
-        if (DELTA && tid < W) bet[tid] = tid < n ? A.bbuf[wbase + tid] : 0.f;
-    }
+    // ---- 3. stage operands ----
     if (sketch) {
+        // basis rows, transposed; consecutive threads write consecutive LDS words
         const float* om = A.basis + size_t(g) * A.basis_rows * K;
-        const int rows = 16 * ((r + 15) / 16);
-        for (int e = tid; e < rows * K; e += NT) {
-            const int m = e / K, kk = e - m * K;
+        const int orows = 16 * ((r + 15) / 16);
+        for (int e = tid; e < orows * K; e += NT) {
+            const int kk = e / orows, m = e - kk * orows;
             OmT[kk * oms + m] = m < r ? om[m * K + kk] : 0.f;
         }
     }
-    __syncthreads();
-
+    float gamW = 1.f;
     if (n > 0) {
-        // 2. running products of the decays
         if (KDA) {
+#pragma unroll
+            for (int j = 0; j < NA; ++j) {
+                const int c = tid + j * NT;
+                if (c < ACH) reinterpret_cast<float4*>(al)[c] = a4[j];
+            }
+            __syncthreads();
             for (int c = tid; c < K; c += NT) {
                 float pr = 1.f;
                 for (int i = 0; i < W; ++i) {
@@ -155,69 +193,75 @@ __global__ __launch_bounds__(V / 16 * 64) void flush_kernel(FlushArgs A, HeadTab
                     sf *= al[i * K + c];
                 }
             }
-        } else if (tid < W) {
-            float pr = 1.f;
-            for (int i = 0; i <= tid; ++i) pr *= al[i];
-            float sf = 1.f;
-            for (int i = tid + 1; i < W; ++i) sf *= al[i];
-            gam[tid] = pr;
-            sig[tid] = sf;
+            __syncthreads();
         }
-        __syncthreads();
-
-        // 3. window keys and values into LDS
-        for (int c = tid; c < W * (K / 8); c += NT) {
-            const int i = c / (K / 8);
-            const int k0 = (c % (K / 8)) * 8;
-            typename V8::raw_t raw = V8::zero();
-            if (i < n) raw = V8::load(A.kbuf, (item * W + i) * K + k0);
+        // prefix / suffix decay products of this thread's key slot (scalar kinds)
+        float gi = 1.f, si = 1.f;
+        if (!KDA) {
+#pragma unroll
+            for (int i = 0; i < W; ++i) {
+                gamW *= as[i];
+                if (i <= ki) gi *= as[i];
+                if (i > ki) si *= as[i];
+            }
+        }
+        if (tid < KCH) {
             float f[8];
-            V8::unpack(raw, f);
+            V8::unpack(kraw, f);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int kk = k0 + e;
-                const float sg = KDA ? sig[i * K + kk] : sig[i];
-                Kt[i * kKtStride + kk] = f[e] * sg;
+                const int kk = kk0 + e;
+                const float sg = KDA ? sig[ki * K + kk] : si;
+                Kt[ki * kKtStride + kk] = f[e] * sg;
                 if (DELTA) {
-                    const float gm = KDA ? gam[i * K + kk] : gam[i];
-                    Kr[i * K + kk] = f[e];
-                    KgT[kk * kKgStride + i] = f[e] * gm;
+                    const float gm = KDA ? gam[ki * K + kk] : gi;
+                    Kr[ki * K + kk] = f[e];
+                    KgT[kk * kKgStride + ki] = f[e] * gm;
                 }
             }
         }
-        for (int c = tid; c < W * (V / 8); c += NT) {
-            const int i = c / (V / 8);
-            const int c0 = (c % (V / 8)) * 8;
-            typename V8::raw_t raw = V8::zero();
-            if (i < n) raw = V8::load(A.vbuf, (item * W + i) * V + c0);
+        if (tid < VCH) {
             float f[8];
-            V8::unpack(raw, f);
+            V8::unpack(vraw, f);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) U[i * US + c0 + e] = f[e];
+            for (int e = 0; e < 8; ++e) U[vi * US + vc0 + e] = f[e];
         }
-        __syncthreads();
+    }
+    __syncthreads();
 
+    if (n > 0) {
         if (DELTA) {
             // 4a. L: row i of 16 lanes handles token i against every earlier token
-            const int i = tid >> 4;
-            const int l16 = tid & 15;
-            if (i >= 1 && i < W) {
-                float ki[8], R[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    ki[e] = Kr[i * K + 8 * l16 + e];
-                    R[e] = 1.f;
-                }
-                const float bi = bet[i];
-                for (int j = i - 1; j >= 0; --j) {
-                    float t = 0.f;
+            {
+                const int i = tid >> 4;
+                const int l16 = tid & 15;
+                if (i >= 1 && i < W) {
+                    float kv[8], R[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) {
-                        R[e] *= KDA ? al[(j + 1) * K + 8 * l16 + e] : al[j + 1];
-                        t = fmaf(ki[e] * R[e], Kr[j * K + 8 * l16 + e], t);
+                        kv[e] = Kr[i * K + 8 * l16 + e];
+                        R[e] = 1.f;
                     }
-                    const float sum = row_sum16(t);
-                    if (l16 == 0) Lm[i * 16 + j] = bi * sum;
+                    float bi = 0.f;
+#pragma unroll
+                    for (int ii = 0; ii < W; ++ii)
+                        if (ii == i) bi = bs[ii];
+                    for (int j = i - 1; j >= 0; --j) {
+                        float aj = 1.f;
+                        if (!KDA) {
+#pragma unroll
+                            for (int ii = 0; ii < W; ++ii)
+                                if (ii == j + 1) aj = as[ii];
+                        }
+                        float t = 0.f;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            R[e] *= KDA ? al[(j + 1) * K + 8 * l16 + e] : aj;
+                            t = fmaf(kv[e] * R[e], Kr[j * K + 8 * l16 + e], t);
+                        }
+                        const float sum = row_sum16(t);
+                        if (l16 == 0) Lm[i * 16 + j] = bi * sum;
+                    }
                 }
             }
             // 4b. G tile for this wave's columns: rows = tokens, K summed in registers
@@ -227,12 +271,14 @@ __global__ __launch_bounds__(V / 16 * 64) void flush_kernel(FlushArgs A, HeadTab
 #pragma unroll
                 for (int ss = 0; ss < 4; ++ss)
                     gacc = mfma_16x16x4(KgT[(16 * kt + 4 * lq + ss) * kKgStride + lr], s[kt][ss], gacc);
-            // U <- beta_i (V_i - G_i) for the wave's own columns
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const int ii = 4 * lq + rr;
-                float* up = U + ii * US + v0 + lr;
-                *up = bet[ii] * (*up - gacc[rr]);
+                float bsel = 0.f;
+#pragma unroll
+                for (int ii = 0; ii < W; ++ii)
+                    if (ii == 4 * lq + rr) bsel = bs[ii];
+                float* up = U + (4 * lq + rr) * US + v0 + lr;
+                *up = bsel * (*up - gacc[rr]);
             }
             __syncthreads();
             // 4c. forward substitution (I + L) U = rhs, one lane per column
@@ -258,7 +304,7 @@ __global__ __launch_bounds__(V / 16 * 64) void flush_kernel(FlushArgs A, HeadTab
             f32x4 acc;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
-                const float gw = KDA ? gam[(W - 1) * K + 16 * kt + 4 * lq + rr] : gam[W - 1];
+                const float gw = KDA ? gam[(W - 1) * K + 16 * kt + 4 * lq + rr] : gamW;
                 acc[rr] = gw * s[kt][rr];
             }
 #pragma unroll
@@ -271,7 +317,7 @@ __global__ __launch_bounds__(V / 16 * 64) void flush_kernel(FlushArgs A, HeadTab
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) Si[(16 * kt + 4 * lq + rr) * V + v0 + lr] = s[kt][rr];
+            for (int rr = 0; rr < 4; ++rr) buffer_store_f32(s[kt][rr], srs, svo, (16 * kt + rr) * V * 4);
     }
 
     // 6. Z = Omega_r S for a sketch head

@@ -1,31 +1,32 @@
 // SketchSSM decode read (sketch heads and dense-fallback heads) for gfx950.
 //
-// One launch serves one decode step of a layer.  Work items are (b, h) pairs.
-// Blocks are laid out along the plan's head order: first one block per item of
-// every dense head (a dense item streams its whole fp32 state, ~21x the bytes
-// of a rank-6 sketch item), then, per sketch head from high rank buckets to
-// low, tiles of 16 batch rows.  Consecutive blocks land on different XCDs, so
-// the heavy dense items spread over the whole chip first.
+// One launch serves one decode step of a layer; work items are (b, h) pairs.
+// Blocks follow the plan's head order: first one block per item of every dense
+// head (a dense item streams its whole fp32 state, ~21x the bytes of a rank-6
+// sketch item), then, per sketch head from high rank buckets to low, blocks of
+// 16 batch rows with one 16-lane DPP row per item.  Consecutive blocks land on
+// different XCDs, so the heavy dense items spread over the chip first.
 //
-// Sketch tile (256 threads, one 16-lane row per item):
-//   * the head's coefficient map F (r x K) is staged once in LDS;
-//   * the row loads q, k, v, decay (and beta) of the current token and appends
-//     them to window slot `pos`;
-//   * it sweeps the window back to the last flush: for the current token and
-//     then slots pos-1 .. 0, s = k_i . u, intra += beta_i s v_i, u <- M_i^T u,
+// Per item the read
+//   * appends the current token (k, v, decay, beta) to window slot `pos`;
+//   * sweeps the window back to the last flush: for the current token and then
+//     slots pos-1 .. 0, s = k_i . u, intra += beta_i s v_i, u <- M_i^T u,
 //     starting at u = q, so that u ends as q~ (page "SketchSSM: Write to the
 //     Full State, Read from a Compact Sketch", Abstract: buffered keys and
 //     values between state updates);
-//   * c_m = F_m . q~ (16-lane DPP reductions) and y = sum_m c_m Z_m + intra
-//     (same Abstract: sketch vectors combined with query-dependent
-//     coefficients, no full-state read).
-// Dense item (256 threads): the state rows are streamed with 16-byte loads
-// issued before the sweep; one row sweeps the window; then y = S_0^T q~ + intra
-// with a fixed-order LDS reduction over the key dim.
+//   * sketch head: c_m = F_m . q~ and y = sum_m c_m Z_m + intra (same
+//     Abstract: sketch vectors combined with query-dependent coefficients, no
+//     full-state read); dense head: y = S_0^T q~ + intra.
 //
-// The key dim is 128 = 16 lanes x 8 elements; a lane owns value columns
-// 8l .. 8l+7 for l < V/8.
+// The read is bound by HBM traffic; what costs time is how the bytes are laid
+// out, not arithmetic.  The window is slot-major ([W][H][B]), so a block's
+// append is one contiguous slab and older slots are read as contiguous runs;
+// the sketch is head-major, so a block reads one contiguous span of Z.  Waves
+// stay at <= 64 VGPRs (Mamba-2, bf16) so eight are resident per SIMD and the
+// per-item round trips overlap across the 128 items each CU owns.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "sketchssm_internal.h"
@@ -48,164 +49,259 @@ struct ReadArgs {
     float* y;
     int B, H, pos;
     int n_dense;       // dense heads lead the order
-    int tiles;         // ceil(B / 16) tiles per sketch head
+    int tiles;         // ceil(B / 16) blocks per sketch head
     int dense_blocks;  // n_dense * B
 };
 
 constexpr int kReadThreads = 256;
-constexpr int kRowsPerTile = kReadThreads / 16;
 
 // ---------------------------------------------------------------------------
-// The window sweep of one item, run by one 16-lane row (lane l owns key
-// elements 8l..8l+7 and, for l < V/8, value elements 8l..8l+7).  Appends the
-// current token to slot pos.  Returns u = q~ and the buffered tokens' term.
+// The item sweep in row layout (one 16-lane row per item; lane l owns key
+// elements 8l .. 8l+7 and, for l < V/8, value elements 8l .. 8l+7).  The
+// window is walked from the current token back to slot 0 in chunks of CH
+// slots.  The kernel keeps each wave small (<= 64 VGPRs) so that eight waves
+// per SIMD are resident: with all of a CU's items in flight at once, the
+// serial round trips of one item hide behind the others.
 // ---------------------------------------------------------------------------
-template <int KIND, int V, typename QT>
-__device__ __forceinline__ void row_sweep(const ReadArgs& A, size_t item, int l, float (&u)[8],
-                                          float (&intra)[8]) {
-    using V8 = Vec8<QT>;
-    constexpr int K = kK;
-    constexpr int W = kW;
-    constexpr int VL = V / 8;  // lanes that own value columns
-    const int pos = A.pos;
-    const bool vl = l < VL;
+__device__ __forceinline__ float dot8_bf16(const uint4& a, const uint4& b) {
+    typedef __bf16 __attribute__((ext_vector_type(2))) bf16x2;
+    float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.x),
+                                              __builtin_bit_cast(bf16x2, b.x), 0.f, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.y), __builtin_bit_cast(bf16x2, b.y), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.z), __builtin_bit_cast(bf16x2, b.z), s, false);
+    s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a.w), __builtin_bit_cast(bf16x2, b.w), s, false);
+    return s;
+}
 
-    // current token
-    const typename V8::raw_t qr = V8::load(A.q, item * K + 8 * l);
-    const typename V8::raw_t kr = V8::load(A.k, item * K + 8 * l);
-    typename V8::raw_t vr = V8::zero();
-    if (vl) vr = V8::load(A.v, item * V + 8 * l);
-    float q[8], kc[8], vc[8];
-    V8::unpack(qr, q);
-    V8::unpack(kr, kc);
-    V8::unpack(vr, vc);
-    float ac[8];
-    float bc = 1.f;
-    if (KIND == SKSSM_KDA) {
-        load8f(A.a + item * K + 8 * l, ac);
+// k . q for two raw 8-vectors of the q/k/v dtype (bf16: packed dot products)
+template <typename QT>
+__device__ __forceinline__ float raw_dot8(const typename Vec8<QT>::raw_t& a, const typename Vec8<QT>::raw_t& b) {
+    if constexpr (std::is_same<QT, Bf16Tag>::value) {
+        return dot8_bf16(a.w, b.w);
     } else {
-        ac[0] = A.a[item];
-    }
-    if (KIND != SKSSM_MAMBA2) bc = A.beta[item];
-
-    // append to slot pos
-    const size_t slot = item * W + pos;
-    V8::store(A.kbuf, slot * K + 8 * l, kr);
-    if (vl) V8::store(A.vbuf, slot * V + 8 * l, vr);
-    if (KIND == SKSSM_KDA) {
-        store8f(A.abuf + slot * K + 8 * l, ac);
-    } else if (l == 0) {
-        A.abuf[slot] = ac[0];
-    }
-    if (KIND != SKSSM_MAMBA2 && l == 0) A.bbuf[slot] = bc;
-
-    if (KIND == SKSSM_MAMBA2) {
-        // Scalar decay: every buffered token sees q scaled by the decays of the
-        // tokens after it, so the dot products k_i . q are independent.
-        float g = ac[0];
-        const float s_cur = row_sum16(dot8(kc, q));
-#pragma unroll
-        for (int e = 0; e < 8; ++e) intra[e] = s_cur * vc[e];
-        for (int i0 = pos - 1; i0 >= 0; i0 -= 4) {
-            typename V8::raw_t kw[4], vw[4];
-            float aw[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int i = i0 - c;
-                kw[c] = V8::zero();
-                vw[c] = V8::zero();
-                aw[c] = 1.f;
-                if (i >= 0) {
-                    const size_t si = item * W + i;
-                    kw[c] = V8::load(A.kbuf, si * K + 8 * l);
-                    if (vl) vw[c] = V8::load(A.vbuf, si * V + 8 * l);
-                    aw[c] = A.abuf[si];
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                float kf[8], vf[8];
-                V8::unpack(kw[c], kf);
-                V8::unpack(vw[c], vf);
-                const float s = row_sum16(dot8(kf, q)) * g;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) intra[e] = fmaf(s, vf[e], intra[e]);
-                g *= aw[c];
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) u[e] = g * q[e];
-    } else {
-        // Delta rule: u <- M_i^T u is a serial chain through the window.
-#pragma unroll
-        for (int e = 0; e < 8; ++e) u[e] = q[e];
-        {
-            const float s = row_sum16(dot8(kc, u));
-            const float bs = bc * s;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) intra[e] = bs * vc[e];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float al = (KIND == SKSSM_KDA) ? ac[e] : ac[0];
-                u[e] = al * fmaf(-bs, kc[e], u[e]);
-            }
-        }
-        for (int i0 = pos - 1; i0 >= 0; i0 -= 4) {
-            typename V8::raw_t kw[4], vw[4];
-            float aw[4][8];
-            float bw[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int i = i0 - c;
-                kw[c] = V8::zero();
-                vw[c] = V8::zero();
-                bw[c] = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) aw[c][e] = 1.f;
-                if (i >= 0) {
-                    const size_t si = item * W + i;
-                    kw[c] = V8::load(A.kbuf, si * K + 8 * l);
-                    if (vl) vw[c] = V8::load(A.vbuf, si * V + 8 * l);
-                    if (KIND == SKSSM_KDA) {
-                        load8f(A.abuf + si * K + 8 * l, aw[c]);
-                    } else {
-                        aw[c][0] = A.abuf[si];
-                    }
-                    bw[c] = A.bbuf[si];
-                }
-            }
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                float kf[8], vf[8];
-                V8::unpack(kw[c], kf);
-                V8::unpack(vw[c], vf);
-                const float s = row_sum16(dot8(kf, u));
-                const float bs = bw[c] * s;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) intra[e] = fmaf(bs, vf[e], intra[e]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float al = (KIND == SKSSM_KDA) ? aw[c][e] : aw[c][0];
-                    u[e] = al * fmaf(-bs, kf[e], u[e]);
-                }
-            }
-        }
+        float x[8], y[8];
+        Vec8<QT>::unpack(a, x);
+        Vec8<QT>::unpack(b, y);
+        return dot8(x, y);
     }
 }
 
-// ---------------------------------------------------------------------------
-// Dense item: y = S_0^T q~ + intra, whole block on one (b, h).
-// Thread t < KG*V4 owns float4 column v4 = t % V4 of key rows kg + KG m.
-// ---------------------------------------------------------------------------
 template <int KIND, int V, typename QT>
-__device__ __forceinline__ void dense_item(const ReadArgs& A, const HeadTable& T, int blk) {
+struct RowSweep {
+    static constexpr bool KDA = KIND == SKSSM_KDA;
+    static constexpr bool DELTA = KIND != SKSSM_MAMBA2;
+    static constexpr int CH = KDA ? 1 : 2;  // window slots per round trip
+    static constexpr int NA = KDA ? 8 : 1;  // decay values per slot and lane
+    using V8 = Vec8<QT>;
+
+    // Sweeps the window of `item`, appends the current token to slot pos.
+    // Mamba-2: u = q~ is returned as (gtot, qr) with q~ = gtot q; delta: u = q~.
+    __device__ __forceinline__ static void run(const ReadArgs& A, int b, int h, int l,
+                                               typename V8::raw_t& qr, float (&u)[8],
+                                               float (&acc)[8], float& gtot) {
+        const int pos = A.pos;
+        const size_t item = size_t(b) * A.H + h;
+        // window slot i of this item: [W][H][B] layout, slot-major
+        auto wslot = [&](int i) { return (size_t(i) * A.H + h) * A.B + b; };
+        const bool vl = l < V / 8;
+        qr = V8::load(A.q, item * kK + 8 * l);
+        const typename V8::raw_t kc = V8::load(A.k, item * kK + 8 * l);
+        typename V8::raw_t vc = V8::zero();
+        if (vl) vc = V8::load(A.v, item * V + 8 * l);
+        float ac[NA];
+        if (KDA) load8f(A.a + item * kK + 8 * l, ac);
+        else ac[0] = A.a[item];
+        const float bc = DELTA ? A.beta[item] : 1.f;
+
+        // append the current token to slot pos
+        {
+            const size_t slot = wslot(pos);
+            V8::store(A.kbuf, slot * kK + 8 * l, kc);
+            if (vl) V8::store(A.vbuf, slot * V + 8 * l, vc);
+            if (KDA) store8f(A.abuf + slot * kK + 8 * l, ac);
+            else if (l == 0) A.abuf[slot] = ac[0];
+            if (DELTA && l == 0) A.bbuf[slot] = bc;
+        }
+
+        float g = 1.f;
+        if (!DELTA) {
+            float vf[8];
+            V8::unpack(vc, vf);
+            const float s = row_sum16(raw_dot8<QT>(kc, qr));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = s * vf[e];
+            g = ac[0];
+        } else {
+            V8::unpack(qr, u);
+            float kf[8], vf[8];
+            V8::unpack(kc, kf);
+            V8::unpack(vc, vf);
+            const float bs = bc * row_sum16(dot8(kf, u));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                acc[e] = bs * vf[e];
+                u[e] = (KDA ? ac[e] : ac[0]) * fmaf(-bs, kf[e], u[e]);
+            }
+        }
+
+        for (int i0 = pos - 1; i0 >= 0; i0 -= CH) {
+            typename V8::raw_t kw[CH], vw[CH];
+            float aw[CH][NA], bw[CH];
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const int i = i0 - j;
+                kw[j] = V8::zero();
+                vw[j] = V8::zero();
+#pragma unroll
+                for (int e = 0; e < NA; ++e) aw[j][e] = 1.f;
+                bw[j] = 0.f;
+                if (i >= 0) {
+                    const size_t si = wslot(i);
+                    kw[j] = V8::load(A.kbuf, si * kK + 8 * l);
+                    if (vl) vw[j] = V8::load(A.vbuf, si * V + 8 * l);
+                    if (KDA) load8f(A.abuf + si * kK + 8 * l, aw[j]);
+                    else aw[j][0] = A.abuf[si];
+                    if (DELTA) bw[j] = A.bbuf[si];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                float vf[8];
+                V8::unpack(vw[j], vf);
+                if (!DELTA) {
+                    const float s = row_sum16(raw_dot8<QT>(kw[j], qr)) * g;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] = fmaf(s, vf[e], acc[e]);
+                    g *= aw[j][0];
+                } else {
+                    float kf[8];
+                    V8::unpack(kw[j], kf);
+                    const float bs = bw[j] * row_sum16(dot8(kf, u));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        acc[e] = fmaf(bs, vf[e], acc[e]);
+                        u[e] = (KDA ? aw[j][e] : aw[j][0]) * fmaf(-bs, kf[e], u[e]);
+                    }
+                }
+            }
+        }
+        gtot = g;
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Sketch block: kRows consecutive batch rows of one sketch head.
+// ---------------------------------------------------------------------------
+constexpr int kRows = kReadThreads / 16;
+
+template <int KIND, int V, typename QT>
+__device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable& T, int sb,
+                                             float4* lds4) {
+    constexpr int K = kK;
+    constexpr int VL = V / 8;
+    constexpr bool M2 = KIND == SKSSM_MAMBA2;
+    using V8 = Vec8<QT>;
+    const float* fmap_s = reinterpret_cast<const float*>(lds4);
+
+    const int tid = threadIdx.x;
+    const int row = tid >> 4;
+    const int l = tid & 15;
+    const int tile = sb / A.tiles;
+    const int p = A.n_dense + tile;
+    const int bt = sb - tile * A.tiles;
+    const int h = T.head[p];
+    const int r = T.rank[p];
+    const size_t frow = T.frow[p];
+    const size_t zrow = T.zrow[p];
+    const int b = bt * kRows + row;
+    const bool active = b < A.B;
+    const size_t item = size_t(b) * A.H + h;
+    const float* Zi = A.Z + (zrow * A.B + size_t(b) * r) * V;
+
+    // the coefficient map straight into LDS (wave w fills 1 KB pieces w, w+4, ...)
+    {
+        const float4* fsrc = reinterpret_cast<const float4*>(A.frames + frow * K);
+        const int n4 = r * (K / 4);
+        const int w = tid >> 6, L = tid & 63;
+        for (int c = w; c * 64 < n4; c += kReadThreads / 64) {
+            const int e = min(c * 64 + L, n4 - 1);
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(fsrc + e),
+                                             (__attribute__((address_space(3))) void*)(lds4 + c * 64),
+                                             16, 0, 0);
+        }
+    }
+
+    typename V8::raw_t qr;
+    float u[8], acc[8], gtot = 1.f;
+    if (active) RowSweep<KIND, V, QT>::run(A, b, h, l, qr, u, acc, gtot);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the map has landed
+    __syncthreads();
+    if (!active) return;
+    if (M2) {
+        float q[8];
+        V8::unpack(qr, q);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) u[e] = gtot * q[e];
+    }
+
+    // y = sum_m (F_m . q~) Z_m + intra, two sketch rows per round trip
+    for (int m = 0; m < r; m += 2) {
+        float z0[8], z1[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            z0[e] = 0.f;
+            z1[e] = 0.f;
+        }
+        if (l < VL) {
+            load8f(Zi + size_t(m) * V + 8 * l, z0);
+            if (m + 1 < r) load8f(Zi + size_t(m + 1) * V + 8 * l, z1);
+        }
+        {
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = fmap_s[m * K + 8 * l + e];
+            const float c0 = row_sum16(dot8(f, u));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(c0, z0[e], acc[e]);
+        }
+        if (m + 1 < r) {
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = fmap_s[(m + 1) * K + 8 * l + e];
+            const float c1 = row_sum16(dot8(f, u));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = fmaf(c1, z1[e], acc[e]);
+        }
+    }
+    if (l < VL) store8f(A.y + item * V + 8 * l, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Dense block: y = S_0^T q~ + intra for one (b, h).  Row 0 sweeps the window
+// while the block streams the state with 16-byte loads, PH rows per thread
+// per round trip; thread t < KG*V4 owns float4 column t % V4 of key rows
+// t / V4 + KG m, summed over the key rows in a fixed order through LDS.
+// ---------------------------------------------------------------------------
+template <int V>
+struct DenseLds {
+    static constexpr int V4 = V / 4;
+    static constexpr int KG = kReadThreads / V4;
+    static constexpr size_t bytes = size_t(kK + V) * 4 + size_t(KG) * V4 * 16;
+};
+
+template <int KIND, int V, typename QT>
+__device__ __forceinline__ void dense_block(const ReadArgs& A, const HeadTable& T, int blk,
+                                            float4* lds4) {
     constexpr int K = kK;
     constexpr int V4 = V / 4;
     constexpr int KG = kReadThreads / V4;
     constexpr int NM = (K + KG - 1) / KG;
-    __shared__ float qt_s[K];
-    __shared__ float intra_s[V];
-    __shared__ float4 part[KG * V4];
+    constexpr int PH = 4;
+    constexpr bool M2 = KIND == SKSSM_MAMBA2;
+    using V8 = Vec8<QT>;
+    float4* part = lds4;                                          // [KG * V4]
+    float* qt_s = reinterpret_cast<float*>(lds4 + KG * V4);       // [K]
+    float* intra_s = qt_s + K;                                    // [V]
 
     const int tid = threadIdx.x;
     const int p = blk / A.B;
@@ -215,42 +311,55 @@ __device__ __forceinline__ void dense_item(const ReadArgs& A, const HeadTable& T
     const int v4 = tid % V4;
     const int kg = tid / V4;
     const bool owner = tid < KG * V4;
-
-    // stream the state rows first; the sweep below overlaps their latency
     const float4* S4 = reinterpret_cast<const float4*>(A.S + item * size_t(K) * V);
-    float4 sreg[NM];
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-        const int kk = kg + KG * m;
-        sreg[m] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (owner && kk < K) sreg[m] = S4[kk * V4 + v4];
-    }
 
+    float4 sreg[PH];
+#pragma unroll
+    for (int j = 0; j < PH; ++j) {
+        const int kk = kg + KG * j;
+        sreg[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (owner && kk < K) sreg[j] = S4[kk * V4 + v4];
+    }
     if (tid < 16) {
-        float u[8], intra[8];
-        row_sweep<KIND, V, QT>(A, item, tid, u, intra);
+        typename V8::raw_t qr;
+        float u[8], acc[8], g = 1.f;
+        RowSweep<KIND, V, QT>::run(A, b, h, tid, qr, u, acc, g);
+        if (M2) {
+            float q[8];
+            V8::unpack(qr, q);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[e] = g * q[e];
+        }
         store8f(qt_s + 8 * tid, u);
-        if (tid < V / 8) store8f(intra_s + 8 * tid, intra);
+        if (tid < V / 8) store8f(intra_s + 8 * tid, acc);
     }
     __syncthreads();
 
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int m0 = 0; m0 < NM; m0 += PH) {
+        if (m0 > 0) {
 #pragma unroll
-    for (int m = 0; m < NM; ++m) {
-        const int kk = kg + KG * m;
-        if (kk < K) {
-            const float qk = qt_s[kk];
-            acc.x = fmaf(qk, sreg[m].x, acc.x);
-            acc.y = fmaf(qk, sreg[m].y, acc.y);
-            acc.z = fmaf(qk, sreg[m].z, acc.z);
-            acc.w = fmaf(qk, sreg[m].w, acc.w);
+            for (int j = 0; j < PH; ++j) {
+                const int kk = kg + KG * (m0 + j);
+                sreg[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (owner && kk < K) sreg[j] = S4[kk * V4 + v4];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < PH; ++j) {
+            const int kk = kg + KG * (m0 + j);
+            if (kk < K) {
+                const float qk = qt_s[kk];
+                acc.x = fmaf(qk, sreg[j].x, acc.x);
+                acc.y = fmaf(qk, sreg[j].y, acc.y);
+                acc.z = fmaf(qk, sreg[j].z, acc.z);
+                acc.w = fmaf(qk, sreg[j].w, acc.w);
+            }
         }
     }
     if (owner) part[kg * V4 + v4] = acc;
     __syncthreads();
     if (tid < V4) {
-        float4 s = make_float4(intra_s[4 * tid], intra_s[4 * tid + 1], intra_s[4 * tid + 2],
-                               intra_s[4 * tid + 3]);
         float4 t = part[tid];
         for (int g = 1; g < KG; ++g) {
             const float4 x = part[g * V4 + tid];
@@ -259,81 +368,30 @@ __device__ __forceinline__ void dense_item(const ReadArgs& A, const HeadTable& T
             t.z += x.z;
             t.w += x.w;
         }
-        s.x += t.x;
-        s.y += t.y;
-        s.z += t.z;
-        s.w += t.w;
+        const float4 s = make_float4(intra_s[4 * tid] + t.x, intra_s[4 * tid + 1] + t.y,
+                                     intra_s[4 * tid + 2] + t.z, intra_s[4 * tid + 3] + t.w);
         reinterpret_cast<float4*>(A.y + item * V)[tid] = s;
     }
 }
 
-// ---------------------------------------------------------------------------
-// Sketch tile: 16 batch rows of one sketch head.
-// ---------------------------------------------------------------------------
+// Waves per SIMD the register budget is sized for: 8 (64 VGPRs) where the
+// sweep fits, 6 (80 VGPRs) for the wider per-channel / fp32 variants.
 template <int KIND, int V, typename QT>
-__device__ __forceinline__ void sketch_tile(const ReadArgs& A, const HeadTable& T, int sb) {
-    constexpr int K = kK;
-    constexpr int VL = V / 8;
-    extern __shared__ float4 fmap_s4[];  // r x K coefficient map
-    const float* fmap_s = reinterpret_cast<const float*>(fmap_s4);
-
-    const int tid = threadIdx.x;
-    const int p = A.n_dense + sb / A.tiles;
-    const int tile = sb - (sb / A.tiles) * A.tiles;
-    const int h = T.head[p];
-    const int r = T.rank[p];
-    const size_t frow = T.frow[p];
-    const size_t zrow = T.zrow[p];
-
-    {
-        const float4* src = reinterpret_cast<const float4*>(A.frames + frow * K);
-        const int n4 = r * (K / 4);
-        for (int e = tid; e < n4; e += kReadThreads) fmap_s4[e] = src[e];
-    }
-
-    const int row = tid >> 4;
-    const int l = tid & 15;
-    const int b = tile * kRowsPerTile + row;
-    const bool active = b < A.B;
-    const size_t item = size_t(b) * A.H + h;
-
-    float u[8], yacc[8];
-    if (active) row_sweep<KIND, V, QT>(A, item, l, u, yacc);
-    __syncthreads();
-    if (!active) return;
-
-    const float* Zi = A.Z + (zrow * A.B + size_t(b) * r) * V;
-    for (int m0 = 0; m0 < r; m0 += 4) {
-        float zr[4][8];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) zr[c][e] = 0.f;
-            if (m0 + c < r && l < VL) load8f(Zi + size_t(m0 + c) * V + 8 * l, zr[c]);
-        }
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            if (m0 + c < r) {
-                float f[8];
-                const float* fr = fmap_s + (m0 + c) * K + 8 * l;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) f[e] = fr[e];
-                const float cm = row_sum16(dot8(f, u));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) yacc[e] = fmaf(cm, zr[c][e], yacc[e]);
-            }
-        }
-    }
-    if (l < VL) store8f(A.y + item * V + 8 * l, yacc);
-}
+struct ReadOccupancy {
+    static constexpr int value =
+        (KIND == SKSSM_MAMBA2 && V <= 80 && std::is_same<QT, Bf16Tag>::value) ? 8 : 6;
+};
 
 template <int KIND, int V, typename QT>
-__global__ __launch_bounds__(kReadThreads) void read_kernel(ReadArgs A, HeadTable T) {
+__global__ __launch_bounds__(kReadThreads)
+__attribute__((amdgpu_waves_per_eu(ReadOccupancy<KIND, V, QT>::value)))
+void read_kernel(ReadArgs A, HeadTable T) {
+    extern __shared__ float4 lds4[];  // coefficient map (sketch) or reduction buffers (dense)
     const int blk = blockIdx.x;
     if (blk < A.dense_blocks) {
-        dense_item<KIND, V, QT>(A, T, blk);
+        dense_block<KIND, V, QT>(A, T, blk, lds4);
     } else {
-        sketch_tile<KIND, V, QT>(A, T, blk - A.dense_blocks);
+        sketch_block<KIND, V, QT>(A, T, blk - A.dense_blocks, lds4);
     }
 }
 
@@ -403,11 +461,15 @@ static sketchssm_status run_read(const sketchssm_shape& sh, const HeadTable& t, 
     A.H = sh.H;
     A.pos = pos;
     A.n_dense = n_dense;
-    A.tiles = (sh.B + kRowsPerTile - 1) / kRowsPerTile;
+    A.tiles = (sh.B + kRows - 1) / kRows;
     A.dense_blocks = n_dense * sh.B;
     const long grid = long(A.dense_blocks) + long(n_sketch) * A.tiles;
     if (grid <= 0 || grid > 0x7fffffffL) return SKSSM_ESHAPE;
-    const size_t lds = size_t(n_sketch > 0 ? max_rank : 0) * kK * sizeof(float);
+    size_t lds = size_t(n_sketch > 0 ? max_rank : 0) * kK * sizeof(float);
+    if (n_dense > 0) {
+        const size_t dl = sh.V == 64 ? DenseLds<64>::bytes : sh.V == 80 ? DenseLds<80>::bytes : DenseLds<128>::bytes;
+        lds = lds > dl ? lds : dl;
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = sh.qkv == SKSSM_BF16
                              ? launch_read_k<Bf16Tag>(sh.kind, sh.V, A, t, int(grid), lds, s)

@@ -62,10 +62,12 @@ class SketchLayer:
             self.frames = _to_device(packed, torch.float32, dev)
         qdt = torch.bfloat16 if qkv == "bf16" else torch.float32
         self.qdtype = qdt
-        self.kbuf = torch.zeros((B, H, W, K), dtype=qdt, device=dev)
-        self.vbuf = torch.zeros((B, H, W, V), dtype=qdt, device=dev)
-        self.abuf = torch.zeros((B, H, W, K) if kind == "kda" else (B, H, W), dtype=torch.float32, device=dev)
-        self.bbuf = torch.zeros((B, H, W), dtype=torch.float32, device=dev) if kind != "mamba2" else None
+        # the window: slot-major [W][H][B][...], so one decode step appends
+        # one contiguous slab and a block's batch rows are adjacent
+        self.kbuf = torch.zeros((W, H, B, K), dtype=qdt, device=dev)
+        self.vbuf = torch.zeros((W, H, B, V), dtype=qdt, device=dev)
+        self.abuf = torch.zeros((W, H, B, K) if kind == "kda" else (W, H, B), dtype=torch.float32, device=dev)
+        self.bbuf = torch.zeros((W, H, B), dtype=torch.float32, device=dev) if kind != "mamba2" else None
         self.y = torch.empty((B, H, V), dtype=torch.float32, device=dev)
 
     # -- inputs ------------------------------------------------------------
