@@ -30,6 +30,38 @@ if ROOT not in sys.path:
 
 METRIC = "per-layer decode µs + achieved HBM GB/s, Nano-9B layer, batch 256, mean rank 6"
 HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "read_kernel_c1_traffic.md")
+READ_SOURCES = [os.path.join(ROOT, "rank_state_read_amd", "csrc", f)
+                for f in ("read.hip", "device_common.h", "sketchssm_internal.h")]
+
+
+def read_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in READ_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config: str):
+    """HBM bytes per read launch from the committed counter summary, if it was
+    taken on this workload and on the read kernel as it is now (same source
+    hash), else None."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    keys = ("workload:", "source_hash:", "hbm_bytes_per_launch:")
+    vals = dict(line.split(":", 1) for line in text.splitlines() if line.startswith(keys))
+    if vals.get("workload", "").strip() != config:
+        return None
+    if vals.get("source_hash", "").strip() != read_source_hash():
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"].strip()))
+    except (KeyError, ValueError):
+        return None
 
 
 # ---------------------------------------------------------------------------
@@ -81,15 +113,16 @@ def step_bytes(cfg, ranks, dense_all=False) -> float:
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on a bounded sample
 # ---------------------------------------------------------------------------
-def cpu_baseline(cfg, wl, n_items: int = 4096):
+def cpu_baseline(cfg, wl, steps=None, n_items: int = 16384):
     from threadpoolctl import threadpool_limits
 
     from oracle import gather_items, items_oracle
     rng = np.random.default_rng(5)
     H = cfg.H
-    per_head = max(1, n_items // H)
+    per_head = max(1, min(cfg.B, n_items // H))
     items = [(int(b), h) for h in range(H) for b in rng.choice(cfg.B, per_head, replace=False)]
-    steps = [wl.step(t) for t in range(cfg.W)]
+    if steps is None:
+        steps = [wl.step(t) for t in range(cfg.W)]
     so = [gather_items(st, items) for st in steps]
     with threadpool_limits(limits=1):
         orc = items_oracle(wl, items)
@@ -115,6 +148,10 @@ def main():
     ap.add_argument("--config", default="c1")
     ap.add_argument("--instances", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="only the warmup and timed decode steps (for counter runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="copy 1 GiB device to device three times (scales the HBM byte counters)")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -123,6 +160,15 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 3}), flush=True)
+        return
 
     from rank_state_read_amd import binding as Bnd
     from rank_state_read_amd.layer import layer_for_workload
@@ -145,9 +191,8 @@ def main():
     lays = [lay0]
     for _ in range(NI - 1):
         lays.append(layer_for_workload(wl, device=dev, S_init=lay0.S))
-    inputs = []
-    for t in range(W):
-        inputs.append(lay0.upload_step(wl.step(t)))
+    host_steps = [wl.step(t) for t in range(W)]
+    inputs = [lay0.upload_step(st) for st in host_steps]
     log(f"inputs generated ({time.time() - t0:.1f}s)")
     dense_plan = Bnd.Plan(lay0.shape, np.zeros(cfg.H, np.int32), wl.groups)
     for L in lays:
@@ -199,6 +244,9 @@ def main():
     ms = timed(lambda: run_steps(K, warm))
     us_step = ms * 1000.0 / K
     log(f"sketch path: {us_step:.2f} us/step over {K} steps")
+    if args.profile:
+        print(json.dumps({"profile_run": True, "us_per_step": round(us_step, 3), "steps": K}), flush=True)
+        return
 
     # ---- the read kernel alone, per window position ---------------------------
     per_pos = []
@@ -250,7 +298,7 @@ def main():
                    "global_batch": cfg.B, "layer_instances": NI, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "read_kernel (sketchssm_decode_read)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(cfg.name),
                      "bytes_per_launch": int(rb_avg), "avg_launch_us": round(read_us, 3)},
         "detail": {
             "read_us_mean": round(read_us, 3),
@@ -273,7 +321,7 @@ def main():
     }
     if not args.no_cpu:
         log("timing the CPU oracle on a sample ...")
-        out["cpu_baseline"] = cpu_baseline(cfg, wl)
+        out["cpu_baseline"] = cpu_baseline(cfg, wl, host_steps)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

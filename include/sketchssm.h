@@ -1,9 +1,9 @@
 /*
  * sketchssm.h -- C ABI of the SketchSSM decode hot path for MI355X (gfx950).
  *
- * SketchSSM keeps writing the full recurrent state of every linear-attention /
- * SSM head, but between periodic exact flushes it answers each decode query
- * from a compact low-rank sketch of that state instead of the state itself
+ * SketchSSM writes every update of a linear-attention / SSM head's recurrent
+ * state in full, and in the stretch between two exact flushes it serves decode
+ * queries from a small low-rank summary of the state rather than the state
  * (page "SketchSSM" (PyPI, sketchssm 0.1.0), opening paragraph; page
  * "SketchSSM: Write to the Full State, Read from a Compact Sketch", Abstract).
  *
@@ -14,10 +14,12 @@
  *             r uses its first r rows (calibration card "SketchSSM calibration:
  *             Nemotron Nano 9B v2", "Contents": basis (27, 8, 79, 128));
  *   frame     the coefficient map F in R^{r x K} of one (group, rank) pair;
- *   sketch    Z = Omega_r S in R^{r x V}, formed when the full state is read
- *             at a flush (Abstract: precompute outputs for the basis vectors);
- *   window    the W tokens (k, v, decay, beta) buffered since the last flush
- *             (Abstract, on buffering keys and values; W = 16 on the card).
+ *   sketch    Z = Omega_r S in R^{r x V}, formed at a flush, the one point where
+ *             the full state is read (Abstract: the basis directions' outputs are
+ *             kept from each state update);
+ *   window    the W tokens (k, v, decay, beta) held back since the last flush
+ *             (Abstract: updates are amortised by holding keys and values back;
+ *             W = 16 on the card).
  * Transitions: Mamba-2  M = a I;  Gated DeltaNet  M = alpha (I - beta k k^T);
  * KDA  M = (I - beta k k^T) diag(alpha).  Update S_t = M_t S_{t-1} + beta k v^T
  * (beta = 1 for Mamba-2).  At window position j the output is
@@ -124,8 +126,8 @@ size_t sketchssm_frame_elems(const sketchssm_plan* plan);
 
 /*
  * Flush: apply window slots 0 .. n_tokens-1 to the state and, in the same pass
- * over S, write the sketch Z = Omega_r S of every sketch head (Abstract: at each
- * state update the full state is read once to precompute the basis outputs).
+ * over S, write the sketch Z = Omega_r S of every sketch head (Abstract: S is
+ * read a single time per update and its products with the basis are stored).
  *   S      device [B,H,K,V] fp32, in/out.  n_tokens = 0 leaves S bitwise
  *          unchanged and only writes Z (the initial sketch after prefill).
  *   Z      device [sketchssm_z_elems] fp32, out; may be NULL when no head has a rank
@@ -150,9 +152,10 @@ sketchssm_status sketchssm_flush(const sketchssm_plan* plan, float* S, float* Z,
  * (pos+1)-th since the last flush).  Appends the token to window slot pos, sweeps
  * the window back to the flush to form q~ and the buffered tokens' exact term,
  * then outputs y = Z^T (F q~) + intra for sketch heads and y = S_0^T q~ + intra
- * for dense heads (Abstract: combine sketch vectors with query-dependent
- * coefficients, no full-state read; PyPI page, "Make a calibration for your
- * model": a head gets a rank or a dense fallback).  Sketch heads never read S.
+ * for dense heads (Abstract: a decode step mixes the stored sketch rows with
+ * weights computed from the query and leaves S untouched; PyPI page, "Make a
+ * calibration for your model": a head gets a rank or a dense fallback).  Sketch
+ * heads never read S.
  *   S       device [B,H,K,V] fp32 state at the last flush (read by dense heads only)
  *   Z       device sketch (see sketchssm_z_elems); may be NULL without sketch heads
  *   frames  device [sketchssm_frame_elems] fp32; may be NULL without sketch heads

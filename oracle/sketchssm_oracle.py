@@ -7,16 +7,16 @@ the ``workloads`` package.
 
 Plain float64 numpy, written for a reader to check against the method by eye:
 
-* SketchSSM keeps updating the full recurrent state, and between periodic exact
-  flushes reads a compact low-rank sketch of it instead of the state itself
+* The recurrent state is always written in full; in the stretch between two
+  exact flushes, reads go to a small low-rank summary of it, not to the state
   ("SketchSSM" package page, opening paragraph).
-* At each state update the full state is read once to precompute the outputs
-  of fixed, offline-chosen basis vectors (the sketch); every later decode step
-  combines those sketch vectors with query-dependent coefficients to form the
-  output without reading the full state ("SketchSSM: Write to the Full State,
-  Read from a Compact Sketch", Abstract).
-* Updates are buffered over a window of W tokens between flushes (same
-  Abstract, on ReplaySSM-style buffering of keys and values; W = 16 in the
+* A state update is the only time the full state is read; it keeps the
+  state's products with a basis chosen offline (the sketch), and each decode
+  step after it forms the output from those stored rows, weighted by numbers
+  taken from the query, with no access to the state ("SketchSSM: Write to the
+  Full State, Read from a Compact Sketch", Abstract).
+* Keys and values are held back over a window of W tokens between flushes
+  (same Abstract, which credits ReplaySSM with the idea; W = 16 in the
   Nemotron Nano 9B v2 calibration card, "Contents" table).
 * Heads may be assigned a dense fallback instead of a rank ("SketchSSM"
   package page, "Make a calibration for your model", allocate stage); such

@@ -6,13 +6,13 @@
 // key rows of them in registers as eight 16x16 MFMA accumulator tiles
 // (lane l, register r <-> S[16 kt + 4 (l/16) + r][16 w + l%16]).  In one pass
 // over the state it
-//   1. applies the window's n buffered tokens (page "SketchSSM: Write to the
-//      Full State, Read from a Compact Sketch", Abstract: buffered keys and
-//      values, periodic exact state updates; W = 16 on the Nemotron Nano 9B v2
+//   1. applies the window's n held-back tokens (page "SketchSSM: Write to the
+//      Full State, Read from a Compact Sketch", Abstract: keys and values wait
+//      for a periodic exact update; W = 16 on the Nemotron Nano 9B v2
 //      calibration card, "Contents"), and
 //   2. emits the sketch Z = Omega_r S of the updated state for a sketch head
-//      (same Abstract: at each state update the full state is read once to
-//      precompute the outputs of the basis vectors).
+//      (same Abstract: the update is the one time S is read, and the basis
+//      directions' outputs are kept from it).
 //
 // The n updates are applied in chunked ("WY") form, with slots 0..n-1,
 // gamma_i = prod_{m<=i} alpha_m and sigma_i = prod_{m>i} alpha_m (per channel

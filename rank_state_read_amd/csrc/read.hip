@@ -12,11 +12,11 @@
 //   * sweeps the window back to the last flush: for the current token and then
 //     slots pos-1 .. 0, s = k_i . u, intra += beta_i s v_i, u <- M_i^T u,
 //     starting at u = q, so that u ends as q~ (page "SketchSSM: Write to the
-//     Full State, Read from a Compact Sketch", Abstract: buffered keys and
-//     values between state updates);
+//     Full State, Read from a Compact Sketch", Abstract: keys and values are
+//     held back between state updates);
 //   * sketch head: c_m = F_m . q~ and y = sum_m c_m Z_m + intra (same
-//     Abstract: sketch vectors combined with query-dependent coefficients, no
-//     full-state read); dense head: y = S_0^T q~ + intra.
+//     Abstract: the stored sketch rows are mixed with weights taken from the
+//     query, S is not touched); dense head: y = S_0^T q~ + intra.
 //
 // The read is bound by HBM traffic; what costs time is how the bytes are laid
 // out, not arithmetic.  The window is slot-major ([W][H][B]), so a block's
