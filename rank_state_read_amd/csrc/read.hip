@@ -96,6 +96,29 @@ struct RowSweep {
 
     // Sweeps the window of `item`, appends the current token to slot pos.
     // Mamba-2: u = q~ is returned as (gtot, qr) with q~ = gtot q; delta: u = q~.
+    // Appends the current token to window slot pos.  Called after the item's
+    // other loads have been consumed: stores count in the same in-order memory
+    // counter as loads, so a store issued ahead of a load would make the wait
+    // for that load also wait for the store.  The token is re-read here (it
+    // was just read, so this hits in L2) rather than held in registers through
+    // the sweep.
+    __device__ __forceinline__ static void append(const ReadArgs& A, int b, int h, int l) {
+        const size_t item = size_t(b) * A.H + h;
+        const typename V8::raw_t kc = V8::load(A.k, item * kK + 8 * l);
+        typename V8::raw_t vc = V8::zero();
+        if (l < V / 8) vc = V8::load(A.v, item * V + 8 * l);
+        float ac[NA];
+        if (KDA) load8f(A.a + item * kK + 8 * l, ac);
+        else ac[0] = A.a[item];
+        const float bc = DELTA ? A.beta[item] : 1.f;
+        const size_t slot = (size_t(A.pos) * A.H + h) * A.B + b;
+        V8::store(A.kbuf, slot * kK + 8 * l, kc);
+        if (l < V / 8) V8::store(A.vbuf, slot * V + 8 * l, vc);
+        if (KDA) store8f(A.abuf + slot * kK + 8 * l, ac);
+        else if (l == 0) A.abuf[slot] = ac[0];
+        if (DELTA && l == 0) A.bbuf[slot] = bc;
+    }
+
     __device__ __forceinline__ static void run(const ReadArgs& A, int b, int h, int l,
                                                typename V8::raw_t& qr, float (&u)[8],
                                                float (&acc)[8], float& gtot) {
@@ -112,16 +135,6 @@ struct RowSweep {
         if (KDA) load8f(A.a + item * kK + 8 * l, ac);
         else ac[0] = A.a[item];
         const float bc = DELTA ? A.beta[item] : 1.f;
-
-        // append the current token to slot pos
-        {
-            const size_t slot = wslot(pos);
-            V8::store(A.kbuf, slot * kK + 8 * l, kc);
-            if (vl) V8::store(A.vbuf, slot * V + 8 * l, vc);
-            if (KDA) store8f(A.abuf + slot * kK + 8 * l, ac);
-            else if (l == 0) A.abuf[slot] = ac[0];
-            if (DELTA && l == 0) A.bbuf[slot] = bc;
-        }
 
         float g = 1.f;
         if (!DELTA) {
@@ -231,9 +244,10 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
         }
     }
 
+    using RS = RowSweep<KIND, V, QT>;
     typename V8::raw_t qr;
     float u[8], acc[8], gtot = 1.f;
-    if (active) RowSweep<KIND, V, QT>::run(A, b, h, l, qr, u, acc, gtot);
+    if (active) RS::run(A, b, h, l, qr, u, acc, gtot);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the map has landed
     __syncthreads();
     if (!active) return;
@@ -274,6 +288,7 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
         }
     }
     if (l < VL) store8f(A.y + item * V + 8 * l, acc);
+    RS::append(A, b, h, l);
 }
 
 // ---------------------------------------------------------------------------
@@ -321,9 +336,10 @@ __device__ __forceinline__ void dense_block(const ReadArgs& A, const HeadTable& 
         if (owner && kk < K) sreg[j] = S4[kk * V4 + v4];
     }
     if (tid < 16) {
+        using RS = RowSweep<KIND, V, QT>;
         typename V8::raw_t qr;
         float u[8], acc[8], g = 1.f;
-        RowSweep<KIND, V, QT>::run(A, b, h, tid, qr, u, acc, g);
+        RS::run(A, b, h, tid, qr, u, acc, g);
         if (M2) {
             float q[8];
             V8::unpack(qr, q);
@@ -332,6 +348,7 @@ __device__ __forceinline__ void dense_block(const ReadArgs& A, const HeadTable& 
         }
         store8f(qt_s + 8 * tid, u);
         if (tid < V / 8) store8f(intra_s + 8 * tid, acc);
+        RS::append(A, b, h, tid);
     }
     __syncthreads();
 
@@ -375,11 +392,11 @@ __device__ __forceinline__ void dense_block(const ReadArgs& A, const HeadTable& 
 }
 
 // Waves per SIMD the register budget is sized for: 8 (64 VGPRs) where the
-// sweep fits, 6 (80 VGPRs) for the wider per-channel / fp32 variants.
+// sweep fits, 5 (96 VGPRs) for the wider per-channel / fp32 variants.
 template <int KIND, int V, typename QT>
 struct ReadOccupancy {
     static constexpr int value =
-        (KIND == SKSSM_MAMBA2 && V <= 80 && std::is_same<QT, Bf16Tag>::value) ? 8 : 6;
+        (KIND == SKSSM_MAMBA2 && V <= 80 && std::is_same<QT, Bf16Tag>::value) ? 8 : 5;
 };
 
 template <int KIND, int V, typename QT>
