@@ -17,19 +17,24 @@
 // The n updates are applied in chunked ("WY") form, with slots 0..n-1,
 // gamma_i = prod_{m<=i} alpha_m and sigma_i = prod_{m>i} alpha_m (per channel
 // for KDA, scalars otherwise; slots >= n act as alpha = 1, k = v = 0, beta = 0):
-//   Mamba-2:  S_n = gamma S_0 + sum_i (sigma_i k_i) v_i^T
-//   delta:    G = (gamma_i * k_i)^T S_0 rows (W x V),
-//             L_il = beta_i sum_c k_i[c] k_l[c] prod_{l<m<=i} alpha_m[c]  (l < i),
-//             (I + L) U = diag(beta) (V_w - G),
-//             S_n = gamma * S_0 + sum_i (sigma_i * k_i) u_i^T.
-// The state tiles serve directly as the B operand of G and Z: the register
-// index r of a tile is used as the 4-wide K step, which only permutes the
-// order of the key sum, and the A operand is read with the same permutation.
+//   Mamba-2:  S_n = gamma_W S_0 + sum_i (sigma_i k_i) v_i^T
+//   delta:    L_il = beta_i sum_c k_i[c] k_l[c] prod_{l<m<=i} alpha_m[c]  (l < i),
+//             T = (I + L)^{-1} diag(beta),
+//             U = T V_w - (T (gamma K)) S_0       (the rows u_i, W x V),
+//             S_n = gamma_W * S_0 + sum_i (sigma_i * k_i) u_i^T.
+// Everything except the two products with S_0 depends on the window alone, so
+// it is formed while the state is still on its way from HBM: L, T, the 16 x K
+// operand -(T (gamma K)) and the 16 x V tile T V_w.  Once the state has landed
+// each wave only runs MFMAs on its own columns -- U (kept in registers, where
+// its accumulator layout is already the B operand of the update), the update,
+// the store, then Z -- with a single barrier, for the basis rows.
 //
-// Latency: the small loads (window, decays, basis rows) are issued before the
-// 40-64 KB state load, so staging them never waits behind the state; scalar
-// decay products are formed per thread from the 16 decays, so Mamba-2 needs a
-// single barrier per item.
+// The state tiles serve directly as the B operand of the products with S: the
+// register index r of a tile is used as the 4-wide K step, which only permutes
+// the order of the key sum, and the A operand is read with the same
+// permutation.  Window tokens enter every 16-deep product in the order
+// 4 (l/16) + step, so one 16 x 16 accumulator (token rows 4 (l/16) + r) feeds
+// the next product without leaving its lane.
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -46,114 +51,152 @@ struct FlushArgs {
     const float* abuf;
     const float* bbuf;
     int B, H, n_tokens, basis_rows;
-    int omt;  // 16-row tiles of the largest rank (the Omega^T stride is 16 omt + 4)
+    int omt;  // 16-row tiles of the largest rank
 };
 
-// LDS row strides chosen so that the MFMA operand reads of a half-wave hit
-// distinct banks: rows read by lanes 16 apart differ by 16 banks.
-constexpr int kKtStride = kK + 16;  // [i][k]
-constexpr int kKgStride = 20;       // [k][i]
-template <int V>
-struct VStride {
-    static constexpr int value = (V % 32 == 16) ? V : V + 16;
-};
-
+// LDS map, in floats.  Row strides are 4 (mod 16) floats: the rows 4 (l/16) + s
+// that the four quarter-waves read then start 16 banks apart.
 template <int KIND, int V>
 struct FlushLds {
     static constexpr bool delta = KIND != SKSSM_MAMBA2;
     static constexpr bool kda = KIND == SKSSM_KDA;
-    static constexpr int US = VStride<V>::value;
-    static constexpr int kt = 0;                                  // [16][kKtStride]
-    static constexpr int u = kt + 16 * kKtStride;                 // [16][US]
-    static constexpr int nd = kda ? 16 * kK : 0;                  // KDA decay arrays
-    static constexpr int alpha = u + 16 * US;
-    static constexpr int gam = alpha + nd;
-    static constexpr int sig = gam + nd;
-    static constexpr int kr = sig + nd;                           // delta: raw k [16][K]
-    static constexpr int kg = kr + (delta ? 16 * kK : 0);         // delta: [K][kKgStride]
-    static constexpr int lm = kg + (delta ? kK * kKgStride : 0);  // delta: L [16][16]
-    static constexpr int om = lm + (delta ? 256 : 0);             // Omega^T [K][16 omt + 4]
-    static size_t bytes(int omt) { return size_t(om + (omt > 0 ? kK * (16 * omt + 4) : 0)) * 4; }
+    static constexpr int KS = kK + 4;                      // rows of K floats
+    static constexpr int VS = V + 4;                       // rows of V floats
+    static constexpr int kt = 0;                           // sigma-scaled keys [16][KS]
+    static constexpr int ap = kt + 16 * KS;                // delta: raw keys, then -T(gamma K) [16][KS]
+    static constexpr int gw = ap + (delta ? 16 * KS : 0);  // KDA: gamma_W per channel [K]
+    static constexpr int vw = gw + (kda ? kK : 0);         // window values [16][VS]
+    static constexpr int kg = vw + 16 * VS;                // delta: gamma-scaled keys [16][KS]
+    static constexpr int lt = kg + (delta ? 16 * KS : 0);  // delta: L transposed [16][16]
+    static constexpr int tm = lt + (delta ? 256 : 0);      // delta: T [16][16]
+    static constexpr int al = tm + (delta ? 256 : 0);      // KDA: decays [16][K]
+    static constexpr int om = al + (kda ? 16 * kK : 0);    // basis rows [16 omt][K], swizzled
+    static size_t bytes(int omt) { return size_t(om + 16 * omt * kK) * 4; }
 };
 
+__device__ __forceinline__ float read_lane(float x, int l) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
+}
+
+// x[i] for a lane-dependent i (a select chain; x is wave-uniform).
+template <int N>
+__device__ __forceinline__ float pick(const float (&x)[N], int i) {
+    float r = 0.f;
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+        if (j == i) r = x[j];
+    return r;
+}
+
+// Occupancy the register budget is sized for: three 512-thread blocks of the
+// V = 128 kernels per CU, four of the 320-thread V = 80 ones.
+constexpr int kFlushWavesPerEu = 6;
+
 template <int KIND, int V, typename QT>
-__global__ __launch_bounds__(V / 16 * 64) void flush_kernel(FlushArgs A, HeadTable T) {
+__global__ __launch_bounds__(V / 16 * 64) __attribute__((amdgpu_waves_per_eu(kFlushWavesPerEu)))
+void flush_kernel(FlushArgs A, HeadTable T) {
     using V8 = Vec8<QT>;
     using L = FlushLds<KIND, V>;
     constexpr int K = kK;
     constexpr int W = kW;
     constexpr int NW = V / 16;
-    constexpr int NT = NW * 64;
     constexpr bool DELTA = L::delta;
     constexpr bool KDA = L::kda;
-    constexpr int US = L::US;
-    constexpr int KCH = W * K / 8;  // 8-element key chunks of the window
-    constexpr int VCH = W * V / 8;  // 8-element value chunks
-    constexpr int ACH = W * K / 4;  // float4 chunks of KDA decays
-    constexpr int NA = (ACH + NT - 1) / NT;
+    constexpr int KS = L::KS;
+    constexpr int VS = L::VS;
+    constexpr int VCH = W * V / 8;  // 8-element value chunks of the window
     extern __shared__ float4 lds4[];
     float* sm = reinterpret_cast<float*>(lds4);
     float* Kt = sm + L::kt;
-    float* U = sm + L::u;
-    float* al = sm + L::alpha;
-    float* gam = sm + L::gam;
-    float* sig = sm + L::sig;
-    float* Kr = sm + L::kr;
-    float* KgT = sm + L::kg;
-    float* Lm = sm + L::lm;
-    float* OmT = sm + L::om;
+    float* Ap = sm + L::ap;
+    float* Gw = sm + L::gw;
+    float* Vw = sm + L::vw;
+    float* Kg = sm + L::kg;
+    float* Lt = sm + L::lt;
+    float* Tm = sm + L::tm;
+    float* Al = sm + L::al;
+    float* Om = sm + L::om;
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
-    const int lr = lane & 15;  // column inside the wave's 16
-    const int lq = lane >> 4;  // 4-row group
+    const int lr = lane & 15;  // column inside the wave's 16 / row of an A operand
+    const int lq = lane >> 4;  // quarter-wave: 4-row group
     const int p = blockIdx.x / A.B;
     const int b = blockIdx.x - p * A.B;
-    const int h = T.head[p];
-    const int r = T.rank[p];
-    const int g = T.group[p];
+    const int h = __builtin_amdgcn_readfirstlane(T.head[p]);
+    const int r = __builtin_amdgcn_readfirstlane(T.rank[p]);
+    const int g = __builtin_amdgcn_readfirstlane(T.group[p]);
     const size_t item = size_t(b) * A.H + h;
     const int n = A.n_tokens;
     const bool sketch = r > 0 && A.Z != nullptr;
-    const int oms = 16 * A.omt + 4;
     const int v0 = 16 * w;
     // window slot i of this item: [W][H][B] layout, slot-major
     auto wslot = [&](int i) { return (size_t(i) * A.H + h) * A.B + b; };
 
-    // ---- 1. small loads first: window chunk, decays, betas ----
+    // ---- 1. window loads into registers, issued first ----
+    // Every slot is fetched (the window always holds W slots) and slots >= n
+    // are masked where the values are used: the loads then need no branches,
+    // which would make them wait before the state load is issued.  Lane l of
+    // every wave fetches slot l % 16's scalar decay and beta; threads below
+    // KCH / VCH fetch one 8-element chunk of the window's keys / values, and
+    // for KDA threads fetch 4-channel chunks of the decays.
+    constexpr int KCH = W * K / 8;
+    constexpr int ACH = W * K / 4;
+    constexpr int NT = NW * 64;
+    constexpr int NA = KDA ? (ACH + NT - 1) / NT : 1;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    float as_l = 1.f, bs_l = 0.f;
     typename V8::raw_t kraw = V8::zero(), vraw = V8::zero();
-    const int ki = tid >> 4, kk0 = (tid & 15) * 8;            // key chunk of this thread
+    float4 a4[NA];
+    const int ki = tid >> 4, kc0 = (tid & 15) * 8;            // key chunk of this thread
     const int vi = tid / (V / 8), vc0 = (tid % (V / 8)) * 8;  // value chunk of this thread
-    float4 a4[KDA ? NA : 1];
-    float as[W], bs[W];
-#pragma unroll
-    for (int i = 0; i < W; ++i) {
-        as[i] = 1.f;
-        bs[i] = 0.f;
-    }
     if (n > 0) {
-        if (tid < KCH && ki < n) kraw = V8::load(A.kbuf, wslot(ki) * K + kk0);
-        if (tid < VCH && vi < n) vraw = V8::load(A.vbuf, wslot(vi) * V + vc0);
+        if (!KDA) as_l = A.abuf[wslot(lane & 15)];
+        if (DELTA) bs_l = A.bbuf[wslot(lane & 15)];
+        if (tid < KCH) kraw = V8::load(A.kbuf, wslot(ki) * K + kc0);
+        if (tid < VCH) vraw = V8::load(A.vbuf, wslot(vi) * V + vc0);
         if (KDA) {
 #pragma unroll
             for (int j = 0; j < NA; ++j) {
                 const int c = tid + j * NT;
-                a4[j] = make_float4(1.f, 1.f, 1.f, 1.f);
-                if (c < ACH && (c >> 5) < n)
-                    a4[j] = *reinterpret_cast<const float4*>(A.abuf + wslot(c >> 5) * K + (c & 31) * 4);
+                if (c < ACH) a4[j] = *reinterpret_cast<const float4*>(A.abuf + wslot(c >> 5) * K + (c & 31) * 4);
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < W; ++i) as[i] = i < n ? A.abuf[wslot(i)] : 1.f;
-        }
-        if (DELTA) {
-#pragma unroll
-            for (int i = 0; i < W; ++i) bs[i] = i < n ? A.bbuf[wslot(i)] : 0.f;
         }
     }
 
-    // ---- 2. the state: this wave's 16 columns, all key rows ----
+    // ---- 2. basis rows, straight into LDS (16-byte granules; granule c of
+    // row m is stored at slot c ^ (m % 16) so that the sixteen rows one A
+    // operand read touches fall in distinct banks).  Rows from r up to the
+    // next multiple of 16 repeat row r - 1: they only feed sketch rows that
+    // are never stored.
+    if (sketch) {
+        const float* om = A.basis + size_t(g) * A.basis_rows * K;
+        const int half_rows = 8 * ((r + 15) >> 4);
+#pragma unroll
+        for (int j = 0; j < (8 * kMaxRank / 16 + NW - 1) / NW; ++j) {
+            const int qd = wu + j * NW;
+            if (qd < half_rows) {
+                const int gi = 64 * qd + lane;
+                const int m = gi >> 5;
+                const int c4 = (gi & 31) ^ (m & 15);
+                const int srow = m < r ? m : r - 1;
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void*)(om + size_t(srow) * K + 4 * c4),
+                    (__attribute__((address_space(3))) void*)(Om + 256 * qd), 16, 0, 0);
+            }
+        }
+    }
+
+    // Window and basis rows first, the state after: while direct-to-LDS loads
+    // are outstanding the memory counter cannot tell loads apart, so every
+    // later wait would wait for the whole state too.  Waiting here for the
+    // small loads (L2 / last-level cache hits) leaves only state loads in
+    // flight during the window-only work below, and the MFMAs on the state
+    // then wait for each load on its own.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+    // ---- 3. the state: this wave's 16 columns, all key rows ----
     const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(A.S + item * size_t(K) * V, K * V * 4);
     const int svo = (4 * lq * V + v0 + lr) * 4;  // this lane's byte offset in a 16-row tile
     f32x4 s[8];
@@ -162,181 +205,222 @@ __global__ __launch_bounds__(V / 16 * 64) void flush_kernel(FlushArgs A, HeadTab
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) s[kt][rr] = buffer_load_f32(srs, svo, (16 * kt + rr) * V * 4);
 
-    // ---- 3. stage operands ----
-    if (sketch) {
-        // basis rows, transposed; consecutive threads write consecutive LDS words
-        const float* om = A.basis + size_t(g) * A.basis_rows * K;
-        const int orows = 16 * ((r + 15) / 16);
-        for (int e = tid; e < orows * K; e += NT) {
-            const int kk = e / orows, m = e - kk * orows;
-            OmT[kk * oms + m] = m < r ? om[m * K + kk] : 0.f;
-        }
+    // ---- 4. window-only work while the state is in flight ----
+    // slots >= n act as alpha = 1, beta = 0, k = v = 0
+    as_l = (lane & 15) < n ? as_l : 1.f;
+    bs_l = (lane & 15) < n ? bs_l : 0.f;
+    float as[W], bs[W];
+#pragma unroll
+    for (int i = 0; i < W; ++i) {
+        as[i] = read_lane(as_l, i);
+        bs[i] = read_lane(bs_l, i);
     }
     float gamW = 1.f;
+    f32x4 u = {0.f, 0.f, 0.f, 0.f};
     if (n > 0) {
-        if (KDA) {
-#pragma unroll
-            for (int j = 0; j < NA; ++j) {
-                const int c = tid + j * NT;
-                if (c < ACH) reinterpret_cast<float4*>(al)[c] = a4[j];
-            }
-            __syncthreads();
-            for (int c = tid; c < K; c += NT) {
-                float pr = 1.f;
-                for (int i = 0; i < W; ++i) {
-                    pr *= al[i * K + c];
-                    gam[i * K + c] = pr;
-                }
-                float sf = 1.f;
-                for (int i = W - 1; i >= 0; --i) {
-                    sig[i * K + c] = sf;
-                    sf *= al[i * K + c];
-                }
-            }
-            __syncthreads();
-        }
-        // prefix / suffix decay products of this thread's key slot (scalar kinds)
-        float gi = 1.f, si = 1.f;
-        if (!KDA) {
-#pragma unroll
-            for (int i = 0; i < W; ++i) {
-                gamW *= as[i];
-                if (i <= ki) gi *= as[i];
-                if (i > ki) si *= as[i];
-            }
-        }
-        if (tid < KCH) {
-            float f[8];
-            V8::unpack(kraw, f);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int kk = kk0 + e;
-                const float sg = KDA ? sig[ki * K + kk] : si;
-                Kt[ki * kKtStride + kk] = f[e] * sg;
-                if (DELTA) {
-                    const float gm = KDA ? gam[ki * K + kk] : gi;
-                    Kr[ki * K + kk] = f[e];
-                    KgT[kk * kKgStride + ki] = f[e] * gm;
-                }
-            }
-        }
         if (tid < VCH) {
             float f[8];
             V8::unpack(vraw, f);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) U[vi * US + vc0 + e] = f[e];
+            for (int e = 0; e < 8; ++e) f[e] = vi < n ? f[e] : 0.f;
+            store8f(Vw + vi * VS + vc0, f);
         }
-    }
-    __syncthreads();
+        if (KDA) {
+            // raw keys and decays to LDS; channel c's prefix / suffix products
+            // are then formed by thread c
+            if (tid < KCH) {
+                float f[8];
+                V8::unpack(kraw, f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] = ki < n ? f[e] : 0.f;
+                store8f(Ap + ki * KS + kc0, f);
+            }
+#pragma unroll
+            for (int j = 0; j < NA; ++j) {
+                const int c = tid + j * NT;
+                if (c < ACH) {
+                    const bool live = (c >> 5) < n;
+                    const float4 v4 = live ? a4[j] : make_float4(1.f, 1.f, 1.f, 1.f);
+                    *reinterpret_cast<float4*>(Al + (c >> 5) * K + (c & 31) * 4) = v4;
+                }
+            }
+            __syncthreads();
+            if (tid < K) {
+                const int c = tid;
+                float gm = 1.f;
+#pragma unroll 4
+                for (int i = 0; i < W; ++i) {
+                    gm *= Al[i * K + c];
+                    Kg[i * KS + c] = Ap[i * KS + c] * gm;
+                }
+                Gw[c] = gm;
+                float sg = 1.f;
+#pragma unroll 4
+                for (int i = W - 1; i >= 0; --i) {
+                    Kt[i * KS + c] = Ap[i * KS + c] * sg;
+                    sg *= Al[i * K + c];
+                }
+            }
+        } else {
+            // scalar decays: this thread's slot's prefix / suffix products
+#pragma unroll
+            for (int i = 0; i < W; ++i) gamW *= as[i];
+            if (tid < KCH) {
+                float gi = 1.f, si = 1.f;
+#pragma unroll
+                for (int i = 0; i < W; ++i) {
+                    if (i <= ki) gi *= as[i];
+                    if (i > ki) si *= as[i];
+                }
+                float f[8], t[8];
+                V8::unpack(kraw, f);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    f[e] = ki < n ? f[e] : 0.f;
+                    t[e] = f[e] * si;
+                }
+                store8f(Kt + ki * KS + kc0, t);
+                if (DELTA) {
+                    store8f(Ap + ki * KS + kc0, f);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) t[e] = f[e] * gi;
+                    store8f(Kg + ki * KS + kc0, t);
+                }
+            }
+        }
+        __syncthreads();
 
-    if (n > 0) {
         if (DELTA) {
-            // 4a. L: row i of 16 lanes handles token i against every earlier token
+            // 4a. L, row i by the 16 lanes of DPP row i (channels 8 l .. 8 l + 7
+            // each), stored transposed: Lt[l][i] = L[i][l]
             {
                 const int i = tid >> 4;
                 const int l16 = tid & 15;
                 if (i >= 1 && i < W) {
-                    float kv[8], R[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        kv[e] = Kr[i * K + 8 * l16 + e];
-                        R[e] = 1.f;
-                    }
-                    float bi = 0.f;
-#pragma unroll
-                    for (int ii = 0; ii < W; ++ii)
-                        if (ii == i) bi = bs[ii];
+                    // kd = k_i * prod_{j<m<=i} alpha_m, one more decay per step
+                    float kd[8];
+                    load8f(Ap + i * KS + 8 * l16, kd);
+                    const float bi = pick(bs, i);
                     for (int j = i - 1; j >= 0; --j) {
-                        float aj = 1.f;
-                        if (!KDA) {
+                        if (KDA) {
+                            float aj[8];
+                            load8f(Al + (j + 1) * K + 8 * l16, aj);
 #pragma unroll
-                            for (int ii = 0; ii < W; ++ii)
-                                if (ii == j + 1) aj = as[ii];
-                        }
-                        float t = 0.f;
+                            for (int e = 0; e < 8; ++e) kd[e] *= aj[e];
+                        } else {
+                            const float aj = pick(as, j + 1);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            R[e] *= KDA ? al[(j + 1) * K + 8 * l16 + e] : aj;
-                            t = fmaf(kv[e] * R[e], Kr[j * K + 8 * l16 + e], t);
+                            for (int e = 0; e < 8; ++e) kd[e] *= aj;
                         }
-                        const float sum = row_sum16(t);
-                        if (l16 == 0) Lm[i * 16 + j] = bi * sum;
+                        float kj[8];
+                        load8f(Ap + j * KS + 8 * l16, kj);
+                        const float sum = row_sum16(dot8(kd, kj));
+                        if (l16 == 0) Lt[j * 16 + i] = bi * sum;
                     }
                 }
-            }
-            // 4b. G tile for this wave's columns: rows = tokens, K summed in registers
-            f32x4 gacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-                for (int ss = 0; ss < 4; ++ss)
-                    gacc = mfma_16x16x4(KgT[(16 * kt + 4 * lq + ss) * kKgStride + lr], s[kt][ss], gacc);
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                float bsel = 0.f;
-#pragma unroll
-                for (int ii = 0; ii < W; ++ii)
-                    if (ii == 4 * lq + rr) bsel = bs[ii];
-                float* up = U + (4 * lq + rr) * US + v0 + lr;
-                *up = bsel * (*up - gacc[rr]);
             }
             __syncthreads();
-            // 4c. forward substitution (I + L) U = rhs, one lane per column
-            if (lane < 16) {
-                const int col = v0 + lane;
-                float uc[W];
+            // 4b. T = (I + L)^{-1} diag(beta): lane c of wave 0 solves column c
+            // (column-oriented forward substitution; L is unit-free strictly lower)
+            if (tid < W) {
+                const int c = tid;
+                const float bc = pick(bs, c);
+                float x[W];
 #pragma unroll
-                for (int ii = 0; ii < W; ++ii) {
-                    float acc = U[ii * US + col];
+                for (int i = 0; i < W; ++i) x[i] = i == c ? bc : 0.f;
 #pragma unroll
-                    for (int jj = 0; jj < ii; ++jj) acc = fmaf(-Lm[ii * 16 + jj], uc[jj], acc);
-                    uc[ii] = acc;
+                for (int l = 0; l < W - 1; ++l) {
+                    const float xl = x[l];
+#pragma unroll
+                    for (int i = l + 1; i < W; ++i) x[i] = fmaf(-Lt[l * 16 + i], xl, x[i]);
                 }
 #pragma unroll
-                for (int ii = 0; ii < W; ++ii) U[ii * US + col] = uc[ii];
+                for (int i = 0; i < W; ++i) Tm[i * 16 + c] = x[i];
+            }
+            __syncthreads();
+            // 4c. u = T V_w on this wave's columns, and -T (gamma K) over all keys
+            float ta[4];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) ta[st] = Tm[lr * 16 + 4 * lq + st];
+#pragma unroll
+            for (int st = 0; st < 4; ++st) u = mfma_16x16x4(ta[st], Vw[(4 * lq + st) * VS + v0 + lr], u);
+            for (int kt = w; kt < 8; kt += NW) {
+                f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int st = 0; st < 4; ++st)
+                    d = mfma_16x16x4(ta[st], Kg[(4 * lq + st) * KS + 16 * kt + lr], d);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) Ap[(4 * lq + rr) * KS + 16 * kt + lr] = -d[rr];
             }
             __syncthreads();
         }
+    }
+    // nothing that reads the state may be scheduled above this point
+    __builtin_amdgcn_sched_barrier(0);
 
-        // 5. S <- gamma * S + Kt^T U, stored back
+    // ---- 5. with the state: U and the update ----
+    if (n > 0) {
+        if (DELTA) {
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt) {
+                const f32x4 a4 = *reinterpret_cast<const f32x4*>(Ap + lr * KS + 16 * kt + 4 * lq);
+#pragma unroll
+                for (int ss = 0; ss < 4; ++ss) u = mfma_16x16x4(a4[ss], s[kt][ss], u);
+            }
+        }
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt) {
             f32x4 acc;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const float gw = KDA ? gam[(W - 1) * K + 16 * kt + 4 * lq + rr] : gamW;
-                acc[rr] = gw * s[kt][rr];
+            if (KDA) {
+                const f32x4 g4 = *reinterpret_cast<const f32x4*>(Gw + 16 * kt + 4 * lq);
+                acc = g4 * s[kt];
+            } else {
+                acc = gamW * s[kt];
             }
 #pragma unroll
             for (int ss = 0; ss < 4; ++ss) {
-                const int ii = 4 * ss + lq;
-                acc = mfma_16x16x4(Kt[ii * kKtStride + 16 * kt + lr], U[ii * US + v0 + lr], acc);
+                const float bop = DELTA ? u[ss] : Vw[(4 * lq + ss) * VS + v0 + lr];
+                acc = mfma_16x16x4(Kt[(4 * lq + ss) * KS + 16 * kt + lr], bop, acc);
             }
             s[kt] = acc;
         }
-#pragma unroll
-        for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) buffer_store_f32(s[kt][rr], srs, svo, (16 * kt + rr) * V * 4);
     }
-
-    // 6. Z = Omega_r S for a sketch head
-    if (sketch) {
+    // ---- 6. Z = Omega_r S for a sketch head, then the state store ----
+    // Z goes first: reading the basis rows makes the compiler wait for every
+    // outstanding memory operation, which at this point are only consumed
+    // state loads, not the stores.  Every wave waited for its own basis
+    // granules before its state load; the first window barrier (or the one
+    // below when there is no window) makes all of them visible.  The two
+    // cases keep separate tails so that no path reaches the stores with a
+    // state load the compiler still counts as outstanding.
+    auto sketch_rows = [&]() {
         float* Zi = A.Z + (size_t(T.zrow[p]) * A.B + size_t(b) * r) * V;
-        const int mts = (r + 15) / 16;
+        const int mts = (r + 15) >> 4;
         for (int mt = 0; mt < mts; ++mt) {
+            const float* orow = Om + (16 * mt + lr) * K;
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kt = 0; kt < 8; ++kt)
+            for (int kt = 0; kt < 8; ++kt) {
+                const f32x4 o = *reinterpret_cast<const f32x4*>(orow + 4 * ((4 * kt + lq) ^ lr));
 #pragma unroll
-                for (int ss = 0; ss < 4; ++ss)
-                    z = mfma_16x16x4(OmT[(16 * kt + 4 * lq + ss) * oms + 16 * mt + lr], s[kt][ss], z);
+                for (int ss = 0; ss < 4; ++ss) z = mfma_16x16x4(o[ss], s[kt][ss], z);
+            }
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
                 const int m = 16 * mt + 4 * lq + rr;
                 if (m < r) Zi[size_t(m) * V + v0 + lr] = z[rr];
             }
         }
+    };
+    if (n > 0) {
+        if (sketch) sketch_rows();
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) buffer_store_f32(s[kt][rr], srs, svo, (16 * kt + rr) * V * 4);
+    } else if (sketch) {
+        __syncthreads();
+        sketch_rows();
     }
 }
 
