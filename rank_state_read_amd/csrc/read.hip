@@ -94,47 +94,71 @@ struct RowSweep {
     static constexpr int NA = KDA ? 8 : 1;  // decay values per slot and lane
     using V8 = Vec8<QT>;
 
-    // Sweeps the window of `item`, appends the current token to slot pos.
-    // Mamba-2: u = q~ is returned as (gtot, qr) with q~ = gtot q; delta: u = q~.
-    // Appends the current token to window slot pos.  Called after the item's
-    // other loads have been consumed: stores count in the same in-order memory
-    // counter as loads, so a store issued ahead of a load would make the wait
-    // for that load also wait for the store.  The token is re-read here (it
-    // was just read, so this hits in L2) rather than held in registers through
-    // the sweep.
-    __device__ __forceinline__ static void append(const ReadArgs& A, int b, int h, int l) {
-        const size_t item = size_t(b) * A.H + h;
-        const typename V8::raw_t kc = V8::load(A.k, item * kK + 8 * l);
+    // Per-item LDS staging of the current token, written when it is first
+    // read and copied to window slot pos after the item's output: the token
+    // is neither held in registers through the sweep nor read from HBM twice.
+    static constexpr int E = V8::kElemBytes;
+    static constexpr int kStageK = 0;                        // raw key, K elements
+    static constexpr int kStageV = kStageK + kK * E;         // raw value, V elements
+    static constexpr int kStageA = kStageV + V * E;          // KDA: K decays (fp32)
+    static constexpr int kStageS = kStageA + (KDA ? kK * 4 : 0);  // scalar decay, beta
+    static constexpr int kStageBytes = kStageS + 16;
+
+    // Appends the current token to window slot pos from the staging copy.
+    // Called after the item's loads have been consumed: stores count in the
+    // same in-order memory counter as loads, so a store issued ahead of a load
+    // would make the wait for that load also wait for the store.
+    __device__ __forceinline__ static void append(const ReadArgs& A, int b, int h, int l,
+                                                  const char* stg) {
+        const float* ss = reinterpret_cast<const float*>(stg + kStageS);
+        const typename V8::raw_t kc = V8::load(stg + kStageK, 8 * l);
         typename V8::raw_t vc = V8::zero();
-        if (l < V / 8) vc = V8::load(A.v, item * V + 8 * l);
-        float ac[NA];
-        if (KDA) load8f(A.a + item * kK + 8 * l, ac);
-        else ac[0] = A.a[item];
-        const float bc = DELTA ? A.beta[item] : 1.f;
+        if (l < V / 8) vc = V8::load(stg + kStageV, 8 * l);
         const size_t slot = (size_t(A.pos) * A.H + h) * A.B + b;
         V8::store(A.kbuf, slot * kK + 8 * l, kc);
         if (l < V / 8) V8::store(A.vbuf, slot * V + 8 * l, vc);
-        if (KDA) store8f(A.abuf + slot * kK + 8 * l, ac);
-        else if (l == 0) A.abuf[slot] = ac[0];
-        if (DELTA && l == 0) A.bbuf[slot] = bc;
+        if (KDA) {
+            float ac[8];
+            load8f(reinterpret_cast<const float*>(stg + kStageA) + 8 * l, ac);
+            store8f(A.abuf + slot * kK + 8 * l, ac);
+        } else if (l == 0) {
+            A.abuf[slot] = ss[0];
+        }
+        if (DELTA && l == 0) A.bbuf[slot] = ss[1];
     }
 
+    // Sweeps the window of `item` and stages the current token in `stg`.
+    // Mamba-2: u = q~ is returned as (gtot, qr) with q~ = gtot q; delta: u = q~.
     __device__ __forceinline__ static void run(const ReadArgs& A, int b, int h, int l,
                                                typename V8::raw_t& qr, float (&u)[8],
-                                               float (&acc)[8], float& gtot) {
+                                               float (&acc)[8], float& gtot, char* stg) {
         const int pos = A.pos;
         const size_t item = size_t(b) * A.H + h;
         // window slot i of this item: [W][H][B] layout, slot-major
         auto wslot = [&](int i) { return (size_t(i) * A.H + h) * A.B + b; };
         const bool vl = l < V / 8;
+        // lanes >= V/8 own no value elements; they re-read lane 0's chunk (in
+        // bounds, never stored) so that no load sits in a divergent branch,
+        // which would make the compiler wait for it at the branch's end
+        const int vo = vl ? 8 * l : 0;
         qr = V8::load(A.q, item * kK + 8 * l);
         const typename V8::raw_t kc = V8::load(A.k, item * kK + 8 * l);
-        typename V8::raw_t vc = V8::zero();
-        if (vl) vc = V8::load(A.v, item * V + 8 * l);
+        const typename V8::raw_t vc = V8::load(A.v, item * V + vo);
         float ac[NA];
         if (KDA) load8f(A.a + item * kK + 8 * l, ac);
         else ac[0] = A.a[item];
         const float bc = DELTA ? A.beta[item] : 1.f;
+        // keep the token's loads together: the staging stores below must not
+        // pull a wait in between them
+        __builtin_amdgcn_sched_barrier(0);
+        V8::store(stg + kStageK, 8 * l, kc);
+        if (vl) V8::store(stg + kStageV, 8 * l, vc);
+        if (KDA) store8f(reinterpret_cast<float*>(stg + kStageA) + 8 * l, ac);
+        if (l == 0) {
+            float* ss = reinterpret_cast<float*>(stg + kStageS);
+            ss[0] = ac[0];
+            ss[1] = bc;
+        }
 
         float g = 1.f;
         if (!DELTA) {
@@ -206,6 +230,7 @@ struct RowSweep {
 // Sketch block: kRows consecutive batch rows of one sketch head.
 // ---------------------------------------------------------------------------
 constexpr int kRows = kReadThreads / 16;
+constexpr int kMapRows = 16;  // coefficient-map rows staged in LDS at a time
 
 template <int KIND, int V, typename QT>
 __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable& T, int sb,
@@ -214,7 +239,11 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
     constexpr int VL = V / 8;
     constexpr bool M2 = KIND == SKSSM_MAMBA2;
     using V8 = Vec8<QT>;
-    const float* fmap_s = reinterpret_cast<const float*>(lds4);
+    using RS = RowSweep<KIND, V, QT>;
+    // LDS: kRows token staging rows, then the coefficient map
+    constexpr int kMapOff4 = kRows * RS::kStageBytes / 16;
+    char* stg = reinterpret_cast<char*>(lds4) + (threadIdx.x >> 4) * RS::kStageBytes;
+    const float* fmap_s = reinterpret_cast<const float*>(lds4 + kMapOff4);
 
     const int tid = threadIdx.x;
     const int row = tid >> 4;
@@ -231,26 +260,27 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
     const size_t item = size_t(b) * A.H + h;
     const float* Zi = A.Z + (zrow * A.B + size_t(b) * r) * V;
 
-    // the coefficient map straight into LDS (wave w fills 1 KB pieces w, w+4, ...)
-    {
-        const float4* fsrc = reinterpret_cast<const float4*>(A.frames + frow * K);
-        const int n4 = r * (K / 4);
+    // the coefficient map straight into LDS, kMapRows rows at a time (wave w
+    // fills 1 KB pieces w, w+4, ...); most heads need a single piece, and the
+    // block's LDS stays small enough for eight resident blocks per CU
+    auto stage_map = [&](int m0) {
+        const float4* fsrc = reinterpret_cast<const float4*>(A.frames + (frow + m0) * K);
+        const int n4 = min(kMapRows, r - m0) * (K / 4);
         const int w = tid >> 6, L = tid & 63;
         for (int c = w; c * 64 < n4; c += kReadThreads / 64) {
             const int e = min(c * 64 + L, n4 - 1);
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(fsrc + e),
-                                             (__attribute__((address_space(3))) void*)(lds4 + c * 64),
+                                             (__attribute__((address_space(3))) void*)(lds4 + kMapOff4 + c * 64),
                                              16, 0, 0);
         }
-    }
+    };
+    stage_map(0);
 
-    using RS = RowSweep<KIND, V, QT>;
     typename V8::raw_t qr;
     float u[8], acc[8], gtot = 1.f;
-    if (active) RS::run(A, b, h, l, qr, u, acc, gtot);
+    if (active) RS::run(A, b, h, l, qr, u, acc, gtot, stg);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the map has landed
     __syncthreads();
-    if (!active) return;
     if (M2) {
         float q[8];
         V8::unpack(qr, q);
@@ -259,36 +289,47 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
     }
 
     // y = sum_m (F_m . q~) Z_m + intra, two sketch rows per round trip
-    for (int m = 0; m < r; m += 2) {
-        float z0[8], z1[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            z0[e] = 0.f;
-            z1[e] = 0.f;
+    for (int m0 = 0; m0 < r; m0 += kMapRows) {
+        if (m0 > 0) {
+            __syncthreads();  // every row is done with the previous piece
+            stage_map(m0);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
         }
-        if (l < VL) {
-            load8f(Zi + size_t(m) * V + 8 * l, z0);
-            if (m + 1 < r) load8f(Zi + size_t(m + 1) * V + 8 * l, z1);
-        }
-        {
-            float f[8];
+        const int mend = min(r, m0 + kMapRows);
+        if (!active) continue;
+        for (int m = m0; m < mend; m += 2) {
+            float z0[8], z1[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] = fmap_s[m * K + 8 * l + e];
-            const float c0 = row_sum16(dot8(f, u));
+            for (int e = 0; e < 8; ++e) {
+                z0[e] = 0.f;
+                z1[e] = 0.f;
+            }
+            if (l < VL) {
+                load8f(Zi + size_t(m) * V + 8 * l, z0);
+                if (m + 1 < mend) load8f(Zi + size_t(m + 1) * V + 8 * l, z1);
+            }
+            {
+                float f[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = fmaf(c0, z0[e], acc[e]);
-        }
-        if (m + 1 < r) {
-            float f[8];
+                for (int e = 0; e < 8; ++e) f[e] = fmap_s[(m - m0) * K + 8 * l + e];
+                const float c0 = row_sum16(dot8(f, u));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) f[e] = fmap_s[(m + 1) * K + 8 * l + e];
-            const float c1 = row_sum16(dot8(f, u));
+                for (int e = 0; e < 8; ++e) acc[e] = fmaf(c0, z0[e], acc[e]);
+            }
+            if (m + 1 < mend) {
+                float f[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc[e] = fmaf(c1, z1[e], acc[e]);
+                for (int e = 0; e < 8; ++e) f[e] = fmap_s[(m + 1 - m0) * K + 8 * l + e];
+                const float c1 = row_sum16(dot8(f, u));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = fmaf(c1, z1[e], acc[e]);
+            }
         }
     }
+    if (!active) return;
     if (l < VL) store8f(A.y + item * V + 8 * l, acc);
-    RS::append(A, b, h, l);
+    RS::append(A, b, h, l, stg);
 }
 
 // ---------------------------------------------------------------------------
@@ -337,9 +378,10 @@ __device__ __forceinline__ void dense_block(const ReadArgs& A, const HeadTable& 
     }
     if (tid < 16) {
         using RS = RowSweep<KIND, V, QT>;
+        char* stg = reinterpret_cast<char*>(lds4) + DenseLds<V>::bytes;
         typename V8::raw_t qr;
         float u[8], acc[8], g = 1.f;
-        RS::run(A, b, h, tid, qr, u, acc, g);
+        RS::run(A, b, h, tid, qr, u, acc, g, stg);
         if (M2) {
             float q[8];
             V8::unpack(qr, q);
@@ -348,7 +390,7 @@ __device__ __forceinline__ void dense_block(const ReadArgs& A, const HeadTable& 
         }
         store8f(qt_s + 8 * tid, u);
         if (tid < V / 8) store8f(intra_s + 8 * tid, acc);
-        RS::append(A, b, h, tid);
+        RS::append(A, b, h, tid, stg);
     }
     __syncthreads();
 
@@ -403,7 +445,7 @@ template <int KIND, int V, typename QT>
 __global__ __launch_bounds__(kReadThreads)
 __attribute__((amdgpu_waves_per_eu(ReadOccupancy<KIND, V, QT>::value)))
 void read_kernel(ReadArgs A, HeadTable T) {
-    extern __shared__ float4 lds4[];  // coefficient map (sketch) or reduction buffers (dense)
+    extern __shared__ float4 lds4[];  // token staging + coefficient map (sketch) or reduction buffers (dense)
     const int blk = blockIdx.x;
     if (blk < A.dense_blocks) {
         dense_block<KIND, V, QT>(A, T, blk, lds4);
@@ -482,9 +524,13 @@ static sketchssm_status run_read(const sketchssm_shape& sh, const HeadTable& t, 
     A.dense_blocks = n_dense * sh.B;
     const long grid = long(A.dense_blocks) + long(n_sketch) * A.tiles;
     if (grid <= 0 || grid > 0x7fffffffL) return SKSSM_ESHAPE;
-    size_t lds = size_t(n_sketch > 0 ? max_rank : 0) * kK * sizeof(float);
+    // per-item token staging (must match RowSweep's layout)
+    const size_t eb = sh.qkv == SKSSM_BF16 ? 2 : 4;
+    const size_t stage = kK * eb + size_t(sh.V) * eb + (sh.kind == SKSSM_KDA ? kK * 4 : 0) + 16;
+    size_t lds = 0;
+    if (n_sketch > 0) lds = kRows * stage + size_t(max_rank < kMapRows ? max_rank : kMapRows) * kK * sizeof(float);
     if (n_dense > 0) {
-        const size_t dl = sh.V == 64 ? DenseLds<64>::bytes : sh.V == 80 ? DenseLds<80>::bytes : DenseLds<128>::bytes;
+        const size_t dl = (sh.V == 64 ? DenseLds<64>::bytes : sh.V == 80 ? DenseLds<80>::bytes : DenseLds<128>::bytes) + stage;
         lds = lds > dl ? lds : dl;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
