@@ -104,6 +104,22 @@ def flush_bytes(cfg, ranks, n_tokens: int, dense_all: bool = False) -> int:
     return total
 
 
+def rmw_bytes(cfg) -> int:
+    """One standard per-token decode launch: the state read and written, the
+    token (q, k, v, decay, beta) in and y out, for every item."""
+    es = 2 if cfg.qkv == "bf16" else 4
+    per_item = 2 * cfg.K * cfg.V * 4 + cfg.K * es + token_bytes(cfg) + cfg.V * 4
+    return cfg.B * cfg.H * per_item
+
+
+def workload_name(cfg, ranks) -> str:
+    nano = cfg.kind == "mamba2" and (cfg.H, cfg.K, cfg.V) == (128, 128, 80)
+    layer = {"mamba2": "Nemotron-Nano-9B-v2-shaped Mamba-2" if nano else "Mamba-2",
+             "gdn": "Gated-DeltaNet-style", "kda": "KDA-style"}[cfg.kind]
+    return (f"{cfg.name}: {layer} layer, B={cfg.B} H={cfg.H} K={cfg.K} V={cfg.V} W={cfg.W}, "
+            f"mean rank {cfg.mean_rank}, {int((ranks == 0).sum())} dense head(s), {cfg.qkv} q/k/v, fp32 state")
+
+
 def step_bytes(cfg, ranks, dense_all=False) -> float:
     W = cfg.W
     rd = np.mean([read_bytes(cfg, ranks, p, dense_all) for p in range(W)])
@@ -271,6 +287,14 @@ def main():
     dense_read_us = timed(lambda: [dense_read(L, p) for p in range(W) for L in lays], reps=2) * 1000.0 / (NI * W)
     dense_flush_us = timed(lambda: [dense_flush(L, W) for L in lays], reps=4) * 1000.0 / NI
 
+    # ---- standard per-token decode: every token reads and writes the state ------
+    def rmw(L, pos):
+        d = inputs[pos]
+        return L.rmw_step(d["q"], d["k"], d["v"], d["a"], d["beta"])
+
+    [rmw(L, 0) for L in lays]
+    rmw_us = timed(lambda: [rmw(L, p) for p in range(W) for L in lays], reps=2) * 1000.0 / (NI * W)
+
     ranks = wl.ranks
     rb = [read_bytes(cfg, ranks, p) for p in range(W)]
     read_GBps = float(np.mean([b / (t * 1e3) for b, t in zip(rb, per_pos)]))
@@ -292,9 +316,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "hbm_GBps": round(sb / (us_step * 1e3), 1),
-        "config": {"workload": f"{cfg.name}: Nemotron-Nano-9B-v2-shaped Mamba-2 layer, B={cfg.B} H={cfg.H} "
-                               f"K={cfg.K} V={cfg.V} W={W}, mean rank {cfg.mean_rank}, "
-                               f"{int((ranks == 0).sum())} dense head(s), bf16 q/k/v, fp32 state",
+        "config": {"workload": workload_name(cfg, ranks),
                    "global_batch": cfg.B, "layer_instances": NI, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": "read_kernel (sketchssm_decode_read)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -317,6 +339,9 @@ def main():
             "dense_flush_us": round(dense_flush_us, 2),
             "read_ratio_dense_over_sketch": round(dense_read_us / read_us, 3),
             "layer_ratio_dense_over_sketch": round(dense_step_us / us_step, 3),
+            "rmw_step_us": round(rmw_us, 2),
+            "rmw_GBps": round(rmw_bytes(cfg) / (rmw_us * 1e3), 1),
+            "ratio_rmw_over_sketch_step": round(rmw_us / us_step, 3),
         },
     }
     if not args.no_cpu:

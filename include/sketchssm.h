@@ -187,6 +187,23 @@ sketchssm_status sketchssm_dense_read(const sketchssm_shape* shape, const float*
                                       void* vbuf, float* abuf, float* bbuf, int32_t pos,
                                       float* y, void* stream);
 
+/*
+ * Standard per-token decode, the baseline that the pages quote their kernel
+ * speedups against ("SketchSSM: Write to the Full State, Read from a Compact
+ * Sketch", Abstract: the standard vLLM decode; read here as the plain
+ * recurrence, which reads and writes the whole state for every token).  For
+ * every (b, h): S <- M S + beta k v^T, then y = S^T q (the updated state).
+ * No window, plan, sketch or basis is involved.
+ *   S       device [B,H,K,V] fp32, in/out
+ *   q, k    device [B,H,K] qkv dtype;  v device [B,H,V] qkv dtype
+ *   a       device [B,H] fp32 (Mamba-2, GDN) or [B,H,K] fp32 (KDA)
+ *   beta    device [B,H] fp32 (GDN, KDA); NULL for Mamba-2
+ *   y       device [B,H,V] fp32, out
+ */
+sketchssm_status sketchssm_rmw_step(const sketchssm_shape* shape, float* S, const void* q,
+                                    const void* k, const void* v, const float* a,
+                                    const float* beta, float* y, void* stream);
+
 /* Static English text for a status code. */
 const char* sketchssm_status_string(sketchssm_status status);
 

@@ -49,6 +49,7 @@ _PROTOS = {
     "sketchssm_flush": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_vp]),
     "sketchssm_decode_read": (c_i32, [c_vp] * 13 + [c_i32, c_vp, c_vp]),
     "sketchssm_dense_read": (c_i32, [ctypes.POINTER(Shape)] + [c_vp] * 10 + [c_i32, c_vp, c_vp]),
+    "sketchssm_rmw_step": (c_i32, [ctypes.POINTER(Shape)] + [c_vp] * 8),
     "sketchssm_status_string": (ctypes.c_char_p, [c_i32]),
 }
 
@@ -175,3 +176,9 @@ def sketchssm_dense_read(shape: Shape, S, q, k, v, a, beta, kbuf, vbuf, abuf, bb
            lib().sketchssm_dense_read(ctypes.byref(shape), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
                                       _ptr(beta), _ptr(kbuf), _ptr(vbuf), _ptr(abuf), _ptr(bbuf),
                                       int(pos), _ptr(y), _stream(stream)))
+
+
+def sketchssm_rmw_step(shape: Shape, S, q, k, v, a, beta, y, stream=None):
+    _check("sketchssm_rmw_step",
+           lib().sketchssm_rmw_step(ctypes.byref(shape), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                    _ptr(beta), _ptr(y), _stream(stream)))

@@ -101,6 +101,12 @@ class SketchLayer:
                                self.bbuf, pos, y, stream)
         return y
 
+    def rmw_step(self, q, k, v, a, beta=None, y=None, stream=None) -> torch.Tensor:
+        """Standard per-token decode on this layer's state (no window, no sketch)."""
+        y = self.y if y is None else y
+        _b.sketchssm_rmw_step(self.shape, self.S, q, k, v, a, beta, y, stream)
+        return y
+
     # -- views ---------------------------------------------------------------
     def z_item(self, b: int, h: int) -> Optional[torch.Tensor]:
         """The (rank x V) sketch rows of item (b, h), or None for a dense head."""

@@ -151,6 +151,19 @@ def test_dense_read_argument_errors():
                                   FAKE, None) == 1
 
 
+def test_rmw_step_argument_errors():
+    L = B.lib()
+    ok = _shape()
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE]            # S q k v a beta y
+    assert L.sketchssm_rmw_step(ctypes.byref(_shape(V=96)), *args, None) == 2
+    assert L.sketchssm_rmw_step(ctypes.byref(ok), *([None] + args[1:]), None) == 1
+    assert L.sketchssm_rmw_step(ctypes.byref(ok), *(args[:5] + [FAKE, FAKE]), None) == 1  # beta with Mamba-2
+    gdn = _shape(kind="gdn", V=128)
+    assert L.sketchssm_rmw_step(ctypes.byref(gdn), *args, None) == 1                       # GDN needs beta
+    assert L.sketchssm_rmw_step(ctypes.byref(ok), *(args[:6] + [FAKE + 4]), None) == 3     # misaligned y
+    assert L.sketchssm_rmw_step(None, *args, None) == 1
+
+
 def test_status_strings():
     for s in range(7):
         assert B.status_string(s)
