@@ -287,6 +287,29 @@ def main():
     dense_read_us = timed(lambda: [dense_read(L, p) for p in range(W) for L in lays], reps=2) * 1000.0 / (NI * W)
     dense_flush_us = timed(lambda: [dense_flush(L, W) for L in lays], reps=4) * 1000.0 / NI
 
+    # ---- continuous batching: staggered window phases ---------------------------
+    # row b sits at window position (b + step) mod W, so every phase is present in
+    # every step; the rows whose window fills are flushed alone in the same step
+    seq_tabs = []
+    for k in range(W):
+        pv = ((np.arange(cfg.B) + k) % W).astype(np.int32)
+        rows = np.nonzero(pv == W - 1)[0].astype(np.int32)
+        seq_tabs.append((torch.from_numpy(pv).to(dev), torch.from_numpy(rows).to(dev),
+                         torch.full((len(rows),), W, dtype=torch.int32, device=dev)))
+
+    def seq_steps(n, s0):
+        for s in range(s0, s0 + n):
+            L = lays[s % NI]
+            k = (s // NI) % W
+            pv, rows, cnt = seq_tabs[k]
+            d = inputs[k]
+            L.read_seq(pv, d["q"], d["k"], d["v"], d["a"], d["beta"])
+            if rows.numel():
+                L.flush_seq(rows, cnt)
+
+    seq_steps(period, 0)
+    seq_step_us = timed(lambda: seq_steps(K, 0)) * 1000.0 / K
+
     # ---- standard per-token decode: every token reads and writes the state ------
     def rmw(L, pos):
         d = inputs[pos]
@@ -339,6 +362,7 @@ def main():
             "dense_flush_us": round(dense_flush_us, 2),
             "read_ratio_dense_over_sketch": round(dense_read_us / read_us, 3),
             "layer_ratio_dense_over_sketch": round(dense_step_us / us_step, 3),
+            "continuous_batching_step_us": round(seq_step_us, 3),
             "rmw_step_us": round(rmw_us, 2),
             "rmw_GBps": round(rmw_bytes(cfg) / (rmw_us * 1e3), 1),
             "ratio_rmw_over_sketch_step": round(rmw_us / us_step, 3),

@@ -177,6 +177,41 @@ sketchssm_status sketchssm_decode_read(const sketchssm_plan* plan, const float* 
                                        float* bbuf, int32_t pos, float* y, void* stream);
 
 /*
+ * Continuous batching: sketchssm_decode_read where every sequence has its own
+ * window position (sequences join, flush and leave at different steps).
+ *   pos     device [B] int32: row b reads and appends at window slot pos[b]
+ *           (0 .. W-1); any other value (e.g. -1) leaves the row idle -- nothing
+ *           of it is read or written and y keeps its previous contents.  The
+ *           array is read on the device, so bad values are not reported; they
+ *           only idle the row.
+ * Other arguments as in sketchssm_decode_read.  The caller flushes a row with
+ * sketchssm_flush_seq after its read at pos[b] = W-1 and restarts it at 0.
+ */
+sketchssm_status sketchssm_decode_read_seq(const sketchssm_plan* plan, const float* S,
+                                           const float* Z, const float* frames, const void* q,
+                                           const void* k, const void* v, const float* a,
+                                           const float* beta, void* kbuf, void* vbuf,
+                                           float* abuf, float* bbuf, const int32_t* pos, float* y,
+                                           void* stream);
+
+/*
+ * Per-sequence flush: sketchssm_flush for the listed batch rows only.
+ *   seqs      device [n_seqs] int32: batch rows, each at most once per call
+ *             (two blocks updating one row's state would race)
+ *   n_tokens  device [n_seqs] int32: held-back tokens of that row's window,
+ *             0 .. W (W after a full window; fewer to close a window early;
+ *             0 after a prefill, forming the row's first sketch with S untouched)
+ *   n_seqs    >= 0; 0 does nothing
+ * kbuf, vbuf, abuf (and bbuf for the delta rule) are required even if every
+ * count is 0, since the counts live on the device.  A listed row outside
+ * 0 .. B-1 or a count outside 0 .. W idles that row's blocks.
+ */
+sketchssm_status sketchssm_flush_seq(const sketchssm_plan* plan, float* S, float* Z,
+                                     const float* basis, const void* kbuf, const void* vbuf,
+                                     const float* abuf, const float* bbuf, const int32_t* seqs,
+                                     const int32_t* n_tokens, int32_t n_seqs, void* stream);
+
+/*
  * Full-state-read baseline: sketchssm_decode_read with every head dense (each
  * query reads S_0; the ReplaySSM-style read that the Abstract contrasts with).
  * Arguments as in sketchssm_decode_read; the shape replaces the plan.

@@ -50,6 +50,8 @@ _PROTOS = {
     "sketchssm_decode_read": (c_i32, [c_vp] * 13 + [c_i32, c_vp, c_vp]),
     "sketchssm_dense_read": (c_i32, [ctypes.POINTER(Shape)] + [c_vp] * 10 + [c_i32, c_vp, c_vp]),
     "sketchssm_rmw_step": (c_i32, [ctypes.POINTER(Shape)] + [c_vp] * 8),
+    "sketchssm_decode_read_seq": (c_i32, [c_vp] * 16),
+    "sketchssm_flush_seq": (c_i32, [c_vp] * 10 + [c_i32, c_vp]),
     "sketchssm_status_string": (ctypes.c_char_p, [c_i32]),
 }
 
@@ -182,3 +184,19 @@ def sketchssm_rmw_step(shape: Shape, S, q, k, v, a, beta, y, stream=None):
     _check("sketchssm_rmw_step",
            lib().sketchssm_rmw_step(ctypes.byref(shape), _ptr(S), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
                                     _ptr(beta), _ptr(y), _stream(stream)))
+
+
+def sketchssm_decode_read_seq(plan: Plan, S, Z, frames, q, k, v, a, beta, kbuf, vbuf, abuf, bbuf, pos,
+                              y, stream=None):
+    _check("sketchssm_decode_read_seq",
+           lib().sketchssm_decode_read_seq(plan.handle, _ptr(S), _ptr(Z), _ptr(frames), _ptr(q), _ptr(k),
+                                           _ptr(v), _ptr(a), _ptr(beta), _ptr(kbuf), _ptr(vbuf),
+                                           _ptr(abuf), _ptr(bbuf), _ptr(pos), _ptr(y), _stream(stream)))
+
+
+def sketchssm_flush_seq(plan: Plan, S, Z, basis, kbuf, vbuf, abuf, bbuf, seqs, n_tokens, n_seqs: int,
+                        stream=None):
+    _check("sketchssm_flush_seq",
+           lib().sketchssm_flush_seq(plan.handle, _ptr(S), _ptr(Z), _ptr(basis), _ptr(kbuf), _ptr(vbuf),
+                                     _ptr(abuf), _ptr(bbuf), _ptr(seqs), _ptr(n_tokens), int(n_seqs),
+                                     _stream(stream)))

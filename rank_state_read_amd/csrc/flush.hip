@@ -50,7 +50,10 @@ struct FlushArgs {
     const void* vbuf;
     const float* abuf;
     const float* bbuf;
+    const int32_t* seqs;  // batch rows to flush (continuous batching) or null: every row
+    const int32_t* ntok;  // tokens held back per listed row
     int B, H, n_tokens, basis_rows;
+    int nb;   // blocks per head: B, or the number of listed rows
     int omt;  // 16-row tiles of the largest rank
 };
 
@@ -122,13 +125,20 @@ void flush_kernel(FlushArgs A, HeadTable T) {
     const int lane = tid & 63;
     const int lr = lane & 15;  // column inside the wave's 16 / row of an A operand
     const int lq = lane >> 4;  // quarter-wave: 4-row group
-    const int p = blockIdx.x / A.B;
-    const int b = blockIdx.x - p * A.B;
+    const int p = blockIdx.x / A.nb;
+    const int j = blockIdx.x - p * A.nb;
+    // batch row and held-back tokens of this block; a listed row outside the
+    // batch or a count outside 0 .. W leaves the block idle
+    int b = j, n = A.n_tokens;
+    if (A.seqs) {
+        b = __builtin_amdgcn_readfirstlane(A.seqs[j]);
+        n = __builtin_amdgcn_readfirstlane(A.ntok[j]);
+        if (b < 0 || b >= A.B || n < 0 || n > W) return;
+    }
     const int h = __builtin_amdgcn_readfirstlane(T.head[p]);
     const int r = __builtin_amdgcn_readfirstlane(T.rank[p]);
     const int g = __builtin_amdgcn_readfirstlane(T.group[p]);
     const size_t item = size_t(b) * A.H + h;
-    const int n = A.n_tokens;
     const bool sketch = r > 0 && A.Z != nullptr;
     const int v0 = 16 * w;
     // window slot i of this item: [W][H][B] layout, slot-major
@@ -468,24 +478,32 @@ static hipError_t launch_flush_k(int kind, int V, const FlushArgs& a, const Head
 
 using namespace skssm;
 
-extern "C" sketchssm_status sketchssm_flush(const sketchssm_plan* plan, float* S, float* Z,
-                                            const float* basis, const void* kbuf,
-                                            const void* vbuf, const float* abuf,
-                                            const float* bbuf, int32_t n_tokens, void* stream) {
+static sketchssm_status run_flush(const sketchssm_plan* plan, float* S, float* Z,
+                                  const float* basis, const void* kbuf, const void* vbuf,
+                                  const float* abuf, const float* bbuf, int32_t n_tokens,
+                                  const int32_t* seqs, const int32_t* ntok, int32_t n_seqs,
+                                  void* stream) {
     if (!plan) return SKSSM_EINVAL;
     const sketchssm_shape& sh = plan->shape;
     const bool delta = sh.kind != SKSSM_MAMBA2;
     const int n_sketch = sh.H - plan->n_dense;
+    const bool listed = seqs != nullptr;
+    // with a list every count is on the device: the window must be there
+    const bool window = listed ? n_seqs > 0 : n_tokens > 0;
     if (!S) return SKSSM_EINVAL;
-    if (n_tokens < 0 || n_tokens > sh.W) return SKSSM_EINVAL;
+    if (!listed && (n_tokens < 0 || n_tokens > sh.W)) return SKSSM_EINVAL;
+    if (listed && (!ntok || n_seqs < 0)) return SKSSM_EINVAL;
     if (n_sketch > 0 && (!Z || !basis)) return SKSSM_EINVAL;
-    if (n_tokens > 0 && (!kbuf || !vbuf || !abuf)) return SKSSM_EINVAL;
-    if (n_tokens > 0 && delta && !bbuf) return SKSSM_EINVAL;
+    if (window && (!kbuf || !vbuf || !abuf)) return SKSSM_EINVAL;
+    if (window && delta && !bbuf) return SKSSM_EINVAL;
     if (!delta && bbuf) return SKSSM_EINVAL;
     const void* ptrs[] = {S, Z, basis, kbuf, vbuf, abuf, bbuf};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return SKSSM_EALIGN;
-    if (n_sketch == 0 && n_tokens == 0) return SKSSM_OK;  // nothing to write
+    if (listed && ((reinterpret_cast<uintptr_t>(seqs) | reinterpret_cast<uintptr_t>(ntok)) & 3u))
+        return SKSSM_EALIGN;
+    if (listed && n_seqs == 0) return SKSSM_OK;
+    if (!listed && n_sketch == 0 && n_tokens == 0) return SKSSM_OK;  // nothing to write
 
     FlushArgs A;
     A.S = S;
@@ -495,16 +513,37 @@ extern "C" sketchssm_status sketchssm_flush(const sketchssm_plan* plan, float* S
     A.vbuf = vbuf;
     A.abuf = abuf;
     A.bbuf = bbuf;
+    A.seqs = seqs;
+    A.ntok = ntok;
     A.B = sh.B;
     A.H = sh.H;
-    A.n_tokens = n_tokens;
+    A.n_tokens = listed ? 0 : n_tokens;
     A.basis_rows = sh.basis_rows;
+    A.nb = listed ? n_seqs : sh.B;
     A.omt = n_sketch > 0 ? (plan->max_rank + 15) / 16 : 0;
-    const long grid = long(sh.B) * sh.H;
+    const long grid = long(A.nb) * sh.H;
     if (grid > 0x7fffffffL) return SKSSM_ESHAPE;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = sh.qkv == SKSSM_BF16
                              ? launch_flush_k<Bf16Tag>(sh.kind, sh.V, A, plan->table, int(grid), s)
                              : launch_flush_k<F32Tag>(sh.kind, sh.V, A, plan->table, int(grid), s);
     return e == hipSuccess ? SKSSM_OK : SKSSM_ELAUNCH;
+}
+
+extern "C" sketchssm_status sketchssm_flush(const sketchssm_plan* plan, float* S, float* Z,
+                                            const float* basis, const void* kbuf,
+                                            const void* vbuf, const float* abuf,
+                                            const float* bbuf, int32_t n_tokens, void* stream) {
+    return run_flush(plan, S, Z, basis, kbuf, vbuf, abuf, bbuf, n_tokens, nullptr, nullptr, 0,
+                     stream);
+}
+
+extern "C" sketchssm_status sketchssm_flush_seq(const sketchssm_plan* plan, float* S, float* Z,
+                                                const float* basis, const void* kbuf,
+                                                const void* vbuf, const float* abuf,
+                                                const float* bbuf, const int32_t* seqs,
+                                                const int32_t* n_tokens, int32_t n_seqs,
+                                                void* stream) {
+    if (!seqs) return SKSSM_EINVAL;
+    return run_flush(plan, S, Z, basis, kbuf, vbuf, abuf, bbuf, 0, seqs, n_tokens, n_seqs, stream);
 }

@@ -47,6 +47,7 @@ struct ReadArgs {
     float* abuf;
     float* bbuf;
     float* y;
+    const int32_t* pos_seq;  // per-sequence window positions (continuous batching) or null
     int B, H, pos;
     int n_dense;       // dense heads lead the order
     int tiles;         // ceil(B / 16) blocks per sketch head
@@ -108,13 +109,13 @@ struct RowSweep {
     // Called after the item's loads have been consumed: stores count in the
     // same in-order memory counter as loads, so a store issued ahead of a load
     // would make the wait for that load also wait for the store.
-    __device__ __forceinline__ static void append(const ReadArgs& A, int b, int h, int l,
+    __device__ __forceinline__ static void append(const ReadArgs& A, int b, int h, int l, int pos,
                                                   const char* stg) {
         const float* ss = reinterpret_cast<const float*>(stg + kStageS);
         const typename V8::raw_t kc = V8::load(stg + kStageK, 8 * l);
         typename V8::raw_t vc = V8::zero();
         if (l < V / 8) vc = V8::load(stg + kStageV, 8 * l);
-        const size_t slot = (size_t(A.pos) * A.H + h) * A.B + b;
+        const size_t slot = (size_t(pos) * A.H + h) * A.B + b;
         V8::store(A.kbuf, slot * kK + 8 * l, kc);
         if (l < V / 8) V8::store(A.vbuf, slot * V + 8 * l, vc);
         if (KDA) {
@@ -129,10 +130,9 @@ struct RowSweep {
 
     // Sweeps the window of `item` and stages the current token in `stg`.
     // Mamba-2: u = q~ is returned as (gtot, qr) with q~ = gtot q; delta: u = q~.
-    __device__ __forceinline__ static void run(const ReadArgs& A, int b, int h, int l,
+    __device__ __forceinline__ static void run(const ReadArgs& A, int b, int h, int l, int pos,
                                                typename V8::raw_t& qr, float (&u)[8],
                                                float (&acc)[8], float& gtot, char* stg) {
-        const int pos = A.pos;
         const size_t item = size_t(b) * A.H + h;
         // window slot i of this item: [W][H][B] layout, slot-major
         auto wslot = [&](int i) { return (size_t(i) * A.H + h) * A.B + b; };
@@ -232,7 +232,7 @@ struct RowSweep {
 constexpr int kRows = kReadThreads / 16;
 constexpr int kMapRows = 16;  // coefficient-map rows staged in LDS at a time
 
-template <int KIND, int V, typename QT>
+template <int KIND, int V, typename QT, bool SEQ>
 __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable& T, int sb,
                                              float4* lds4) {
     constexpr int K = kK;
@@ -256,7 +256,10 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
     const size_t frow = T.frow[p];
     const size_t zrow = T.zrow[p];
     const int b = bt * kRows + row;
-    const bool active = b < A.B;
+    // window position of this row's sequence; rows outside the batch, or whose
+    // position is outside 0 .. W-1, do nothing
+    const int pos = SEQ ? (b < A.B ? A.pos_seq[b] : -1) : A.pos;
+    const bool active = b < A.B && pos >= 0 && pos < kW;
     const size_t item = size_t(b) * A.H + h;
     const float* Zi = A.Z + (zrow * A.B + size_t(b) * r) * V;
 
@@ -278,7 +281,7 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
 
     typename V8::raw_t qr;
     float u[8], acc[8], gtot = 1.f;
-    if (active) RS::run(A, b, h, l, qr, u, acc, gtot, stg);
+    if (active) RS::run(A, b, h, l, pos, qr, u, acc, gtot, stg);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the map has landed
     __syncthreads();
     if (M2) {
@@ -329,7 +332,7 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
     }
     if (!active) return;
     if (l < VL) store8f(A.y + item * V + 8 * l, acc);
-    RS::append(A, b, h, l, stg);
+    RS::append(A, b, h, l, pos, stg);
 }
 
 // ---------------------------------------------------------------------------
@@ -345,7 +348,7 @@ struct DenseLds {
     static constexpr size_t bytes = size_t(kK + V) * 4 + size_t(KG) * V4 * 16;
 };
 
-template <int KIND, int V, typename QT>
+template <int KIND, int V, typename QT, bool SEQ>
 __device__ __forceinline__ void dense_block(const ReadArgs& A, const HeadTable& T, int blk,
                                             float4* lds4) {
     constexpr int K = kK;
@@ -364,6 +367,11 @@ __device__ __forceinline__ void dense_block(const ReadArgs& A, const HeadTable& 
     const int b = blk - p * A.B;
     const int h = T.head[p];
     const size_t item = size_t(b) * A.H + h;
+    int pos = A.pos;
+    if (SEQ) {
+        pos = __builtin_amdgcn_readfirstlane(A.pos_seq[b]);
+        if (pos < 0 || pos >= kW) return;  // the whole block: this sequence is idle
+    }
     const int v4 = tid % V4;
     const int kg = tid / V4;
     const bool owner = tid < KG * V4;
@@ -381,7 +389,7 @@ __device__ __forceinline__ void dense_block(const ReadArgs& A, const HeadTable& 
         char* stg = reinterpret_cast<char*>(lds4) + DenseLds<V>::bytes;
         typename V8::raw_t qr;
         float u[8], acc[8], g = 1.f;
-        RS::run(A, b, h, tid, qr, u, acc, g, stg);
+        RS::run(A, b, h, tid, pos, qr, u, acc, g, stg);
         if (M2) {
             float q[8];
             V8::unpack(qr, q);
@@ -390,7 +398,7 @@ __device__ __forceinline__ void dense_block(const ReadArgs& A, const HeadTable& 
         }
         store8f(qt_s + 8 * tid, u);
         if (tid < V / 8) store8f(intra_s + 8 * tid, acc);
-        RS::append(A, b, h, tid, stg);
+        RS::append(A, b, h, tid, pos, stg);
     }
     __syncthreads();
 
@@ -441,16 +449,18 @@ struct ReadOccupancy {
         (KIND == SKSSM_MAMBA2 && V <= 80 && std::is_same<QT, Bf16Tag>::value) ? 8 : 5;
 };
 
-template <int KIND, int V, typename QT>
+// SEQ: every sequence has its own window position (continuous batching);
+// otherwise the whole batch is at position A.pos.
+template <int KIND, int V, typename QT, bool SEQ>
 __global__ __launch_bounds__(kReadThreads)
 __attribute__((amdgpu_waves_per_eu(ReadOccupancy<KIND, V, QT>::value)))
 void read_kernel(ReadArgs A, HeadTable T) {
     extern __shared__ float4 lds4[];  // token staging + coefficient map (sketch) or reduction buffers (dense)
     const int blk = blockIdx.x;
     if (blk < A.dense_blocks) {
-        dense_block<KIND, V, QT>(A, T, blk, lds4);
+        dense_block<KIND, V, QT, SEQ>(A, T, blk, lds4);
     } else {
-        sketch_block<KIND, V, QT>(A, T, blk - A.dense_blocks, lds4);
+        sketch_block<KIND, V, QT, SEQ>(A, T, blk - A.dense_blocks, lds4);
     }
 }
 
@@ -460,7 +470,10 @@ void read_kernel(ReadArgs A, HeadTable T) {
 template <int KIND, int V, typename QT>
 static hipError_t launch_read_t(const ReadArgs& a, const HeadTable& t, int grid, size_t lds,
                                 hipStream_t s) {
-    hipLaunchKernelGGL((read_kernel<KIND, V, QT>), dim3(grid), dim3(kReadThreads), lds, s, a, t);
+    if (a.pos_seq)
+        hipLaunchKernelGGL((read_kernel<KIND, V, QT, true>), dim3(grid), dim3(kReadThreads), lds, s, a, t);
+    else
+        hipLaunchKernelGGL((read_kernel<KIND, V, QT, false>), dim3(grid), dim3(kReadThreads), lds, s, a, t);
     return hipGetLastError();
 }
 
@@ -490,14 +503,16 @@ static sketchssm_status run_read(const sketchssm_shape& sh, const HeadTable& t, 
                                  int max_rank, const float* S, const float* Z, const float* frames,
                                  const void* q, const void* k, const void* v, const float* a,
                                  const float* beta, void* kbuf, void* vbuf, float* abuf,
-                                 float* bbuf, int32_t pos, float* y, void* stream) {
+                                 float* bbuf, int32_t pos, const int32_t* pos_seq, float* y,
+                                 void* stream) {
     const bool delta = sh.kind != SKSSM_MAMBA2;
     const int n_sketch = sh.H - n_dense;
     if (!q || !k || !v || !a || !kbuf || !vbuf || !abuf || !y) return SKSSM_EINVAL;
     if (delta != (beta != nullptr) || delta != (bbuf != nullptr)) return SKSSM_EINVAL;
     if (n_dense > 0 && !S) return SKSSM_EINVAL;
     if (n_sketch > 0 && (!Z || !frames)) return SKSSM_EINVAL;
-    if (pos < 0 || pos >= sh.W) return SKSSM_EINVAL;
+    if (!pos_seq && (pos < 0 || pos >= sh.W)) return SKSSM_EINVAL;
+    if (pos_seq && (reinterpret_cast<uintptr_t>(pos_seq) & 3u)) return SKSSM_EALIGN;
     const void* ptrs[] = {S, Z, frames, q, k, v, a, beta, kbuf, vbuf, abuf, bbuf, y};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return SKSSM_EALIGN;
@@ -519,6 +534,7 @@ static sketchssm_status run_read(const sketchssm_shape& sh, const HeadTable& t, 
     A.B = sh.B;
     A.H = sh.H;
     A.pos = pos;
+    A.pos_seq = pos_seq;
     A.n_dense = n_dense;
     A.tiles = (sh.B + kRows - 1) / kRows;
     A.dense_blocks = n_dense * sh.B;
@@ -552,7 +568,7 @@ extern "C" sketchssm_status sketchssm_decode_read(const sketchssm_plan* plan, co
                                                   int32_t pos, float* y, void* stream) {
     if (!plan) return SKSSM_EINVAL;
     return run_read(plan->shape, plan->table, plan->n_dense, plan->max_rank, S, Z, frames, q, k,
-                    v, a, beta, kbuf, vbuf, abuf, bbuf, pos, y, stream);
+                    v, a, beta, kbuf, vbuf, abuf, bbuf, pos, nullptr, y, stream);
 }
 
 extern "C" sketchssm_status sketchssm_dense_read(const sketchssm_shape* shape, const float* S,
@@ -565,5 +581,16 @@ extern "C" sketchssm_status sketchssm_dense_read(const sketchssm_shape* shape, c
     HeadTable t;
     dense_table(*shape, &t);
     return run_read(*shape, t, shape->H, 0, S, nullptr, nullptr, q, k, v, a, beta, kbuf, vbuf,
-                    abuf, bbuf, pos, y, stream);
+                    abuf, bbuf, pos, nullptr, y, stream);
+}
+
+extern "C" sketchssm_status sketchssm_decode_read_seq(const sketchssm_plan* plan, const float* S,
+                                                      const float* Z, const float* frames,
+                                                      const void* q, const void* k, const void* v,
+                                                      const float* a, const float* beta, void* kbuf,
+                                                      void* vbuf, float* abuf, float* bbuf,
+                                                      const int32_t* pos, float* y, void* stream) {
+    if (!plan || !pos) return SKSSM_EINVAL;
+    return run_read(plan->shape, plan->table, plan->n_dense, plan->max_rank, S, Z, frames, q, k,
+                    v, a, beta, kbuf, vbuf, abuf, bbuf, 0, pos, y, stream);
 }

@@ -101,6 +101,18 @@ class SketchLayer:
                                self.bbuf, pos, y, stream)
         return y
 
+    def read_seq(self, pos, q, k, v, a, beta=None, y=None, stream=None) -> torch.Tensor:
+        """Decode read with a window position per sequence (device int32 [B]; -1 idles a row)."""
+        y = self.y if y is None else y
+        _b.sketchssm_decode_read_seq(self.plan, self.S, self.Z, self.frames, q, k, v, a, beta, self.kbuf,
+                                    self.vbuf, self.abuf, self.bbuf, pos, y, stream)
+        return y
+
+    def flush_seq(self, seqs, n_tokens, stream=None):
+        """Flush the listed sequences (device int32 rows and per-row token counts)."""
+        _b.sketchssm_flush_seq(self.plan, self.S, self.Z, self.basis, self.kbuf, self.vbuf, self.abuf,
+                              self.bbuf, seqs, n_tokens, int(seqs.numel()), stream)
+
     def rmw_step(self, q, k, v, a, beta=None, y=None, stream=None) -> torch.Tensor:
         """Standard per-token decode on this layer's state (no window, no sketch)."""
         y = self.y if y is None else y

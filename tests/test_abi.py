@@ -164,6 +164,26 @@ def test_rmw_step_argument_errors():
     assert L.sketchssm_rmw_step(None, *args, None) == 1
 
 
+def test_seq_entry_points_argument_errors():
+    L = B.lib()
+    plan = B.Plan(_shape(), np.full(8, 6, np.int32), np.repeat(np.arange(2, dtype=np.int32), 4))
+    h = plan.handle
+    rd = [FAKE] * 12                                                  # S Z frames q k v a beta kbuf vbuf abuf bbuf
+    rd[7] = None
+    rd[11] = None                                                     # Mamba-2: no beta, no bbuf
+    assert L.sketchssm_decode_read_seq(h, *rd, None, FAKE, None) == 1  # no positions
+    assert L.sketchssm_decode_read_seq(None, *rd, FAKE, FAKE, None) == 1
+    assert L.sketchssm_decode_read_seq(h, *rd, FAKE + 2, FAKE, None) == 3  # misaligned positions
+    fl = [FAKE] * 7                                                    # S Z basis kbuf vbuf abuf bbuf
+    fl[6] = None
+    assert L.sketchssm_flush_seq(h, *fl, None, FAKE, 1, None) == 1     # no row list
+    assert L.sketchssm_flush_seq(h, *fl, FAKE, None, 1, None) == 1     # no counts
+    assert L.sketchssm_flush_seq(h, *fl, FAKE, FAKE, -1, None) == 1    # negative length
+    assert L.sketchssm_flush_seq(h, *(fl[:3] + [None] + fl[4:]), FAKE, FAKE, 1, None) == 1  # window needed
+    assert L.sketchssm_flush_seq(h, *fl, FAKE, FAKE, 0, None) == 0     # empty list: nothing to do
+    assert L.sketchssm_flush_seq(h, *fl, FAKE + 2, FAKE, 1, None) == 3
+
+
 def test_status_strings():
     for s in range(7):
         assert B.status_string(s)
