@@ -287,12 +287,14 @@ def main():
     dense_read_us = timed(lambda: [dense_read(L, p) for p in range(W) for L in lays], reps=2) * 1000.0 / (NI * W)
     dense_flush_us = timed(lambda: [dense_flush(L, W) for L in lays], reps=4) * 1000.0 / NI
 
-    # ---- continuous batching: staggered window phases ---------------------------
-    # row b sits at window position (b + step) mod W, so every phase is present in
-    # every step; the rows whose window fills are flushed alone in the same step
+    # ---- continuous batching: every sequence at its own window phase -----------
+    # row b started at a random step, so it sits at window position
+    # (phase_b + step) mod W; the rows whose window fills are flushed alone in
+    # the same step
+    phase = np.random.default_rng(11).integers(0, W, size=cfg.B)
     seq_tabs = []
     for k in range(W):
-        pv = ((np.arange(cfg.B) + k) % W).astype(np.int32)
+        pv = ((phase + k) % W).astype(np.int32)
         rows = np.nonzero(pv == W - 1)[0].astype(np.int32)
         seq_tabs.append((torch.from_numpy(pv).to(dev), torch.from_numpy(rows).to(dev),
                          torch.full((len(rows),), W, dtype=torch.int32, device=dev)))

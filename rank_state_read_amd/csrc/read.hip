@@ -281,9 +281,19 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
 
     typename V8::raw_t qr;
     float u[8], acc[8], gtot = 1.f;
-    if (active) RS::run(A, b, h, l, pos, qr, u, acc, gtot, stg);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the map has landed
-    __syncthreads();
+    if (SEQ) {
+        // rows of one tile may sit at different window positions: wait for the
+        // map first, so that no barrier after the sweeps holds every wave to
+        // the tile's longest window
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the map has landed
+        __syncthreads();
+        if (active) RS::run(A, b, h, l, pos, qr, u, acc, gtot, stg);
+    } else {
+        // the map arrives while the sweep runs
+        if (active) RS::run(A, b, h, l, pos, qr, u, acc, gtot, stg);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the map has landed
+        __syncthreads();
+    }
     if (M2) {
         float q[8];
         V8::unpack(qr, q);
@@ -512,7 +522,7 @@ static sketchssm_status run_read(const sketchssm_shape& sh, const HeadTable& t, 
     if (n_dense > 0 && !S) return SKSSM_EINVAL;
     if (n_sketch > 0 && (!Z || !frames)) return SKSSM_EINVAL;
     if (!pos_seq && (pos < 0 || pos >= sh.W)) return SKSSM_EINVAL;
-    if (pos_seq && (reinterpret_cast<uintptr_t>(pos_seq) & 3u)) return SKSSM_EALIGN;
+    if (reinterpret_cast<uintptr_t>(pos_seq) & 3u) return SKSSM_EALIGN;
     const void* ptrs[] = {S, Z, frames, q, k, v, a, beta, kbuf, vbuf, abuf, bbuf, y};
     for (const void* ptr : ptrs)
         if (ptr && !aligned16(ptr)) return SKSSM_EALIGN;

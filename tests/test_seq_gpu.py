@@ -128,6 +128,6 @@ def _run(name, B, T):
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("name,B", [("c1", 20), ("c3", 19), ("c4", 19), ("c0", 2)])
+@pytest.mark.parametrize("name,B", [("c1", 20), ("c1", 37), ("c3", 19), ("c4", 19), ("c0", 2)])
 def test_staggered_windows(name, B):
     _run(name, B, 2 * CONFIGS[name].W + 9)
