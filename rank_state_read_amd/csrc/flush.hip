@@ -1,7 +1,8 @@
 // SketchSSM flush + sketch for gfx950.
 //
 // One block per (b, h) item; consecutive blocks walk the batch of one head, so
-// the head's basis rows stay in L2.  The block has V/16 waves; wave w owns
+// the head's basis rows stay in L2.  With a row list (continuous batching)
+// the blocks walk the listed rows instead, each with its own token count.  The block has V/16 waves; wave w owns
 // value columns 16w .. 16w+15 of the item's fp32 state and holds all K = 128
 // key rows of them in registers as eight 16x16 MFMA accumulator tiles
 // (lane l, register r <-> S[16 kt + 4 (l/16) + r][16 w + l%16]).  In one pass

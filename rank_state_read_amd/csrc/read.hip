@@ -24,6 +24,10 @@
 // the sketch is head-major, so a block reads one contiguous span of Z.  Waves
 // stay at <= 64 VGPRs (Mamba-2, bf16) so eight are resident per SIMD and the
 // per-item round trips overlap across the 128 items each CU owns.
+//
+// A second instance of the kernel (continuous batching) takes one window
+// position per batch row instead of one per launch; a row whose position is
+// outside 0 .. W-1 is left idle.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
