@@ -67,19 +67,26 @@ def measured_traffic(config: str):
 # ---------------------------------------------------------------------------
 # algorithmic bytes (what the method has to move; no re-reads)
 # ---------------------------------------------------------------------------
-def token_bytes(cfg) -> int:
-    """One token of the window: k, v, its decay (vector for KDA) and beta."""
+def _share(cfg) -> int:
+    """Heads sharing one key/query head (1 unless keys and queries are grouped)."""
+    return cfg.H // (cfg.kq_heads or cfg.H)
+
+
+def token_bytes(cfg) -> float:
+    """One token of the window per head: k (a shared key counted once per
+    group), v, its decay (vector for KDA) and beta."""
     es = 2 if cfg.qkv == "bf16" else 4
     a = 4 * cfg.K if cfg.kind == "kda" else 4
     b = 4 if cfg.kind != "mamba2" else 0
-    return (cfg.K + cfg.V) * es + a + b
+    return cfg.K * es / _share(cfg) + cfg.V * es + a + b
 
 
 def read_bytes(cfg, ranks, pos: int, dense_all: bool = False) -> int:
     """Bytes of one read launch at window position pos (0-based)."""
     es = 2 if cfg.qkv == "bf16" else 4
     tb = token_bytes(cfg)
-    per_item_common = cfg.K * es + tb + tb + pos * tb + cfg.V * 4  # q + (k,v,a,b in) + append + window + y
+    # q + (k,v,a,b in) + append + window + y
+    per_item_common = cfg.K * es / _share(cfg) + tb + tb + pos * tb + cfg.V * 4
     total = 0
     frames_rows = set()
     for h in range(cfg.H):
@@ -108,16 +115,18 @@ def rmw_bytes(cfg) -> int:
     """One standard per-token decode launch: the state read and written, the
     token (q, k, v, decay, beta) in and y out, for every item."""
     es = 2 if cfg.qkv == "bf16" else 4
-    per_item = 2 * cfg.K * cfg.V * 4 + cfg.K * es + token_bytes(cfg) + cfg.V * 4
-    return cfg.B * cfg.H * per_item
+    per_item = 2 * cfg.K * cfg.V * 4 + cfg.K * es / _share(cfg) + token_bytes(cfg) + cfg.V * 4
+    return int(cfg.B * cfg.H * per_item)
 
 
 def workload_name(cfg, ranks) -> str:
     nano = cfg.kind == "mamba2" and (cfg.H, cfg.K, cfg.V) == (128, 128, 80)
     layer = {"mamba2": "Nemotron-Nano-9B-v2-shaped Mamba-2" if nano else "Mamba-2",
              "gdn": "Gated-DeltaNet-style", "kda": "KDA-style"}[cfg.kind]
+    shared = f", q/k shared by {_share(cfg)} heads" if _share(cfg) > 1 else ""
     return (f"{cfg.name}: {layer} layer, B={cfg.B} H={cfg.H} K={cfg.K} V={cfg.V} W={cfg.W}, "
-            f"mean rank {cfg.mean_rank}, {int((ranks == 0).sum())} dense head(s), {cfg.qkv} q/k/v, fp32 state")
+            f"mean rank {cfg.mean_rank}, {int((ranks == 0).sum())} dense head(s), {cfg.qkv} q/k/v, fp32 state"
+            f"{shared}")
 
 
 def step_bytes(cfg, ranks, dense_all=False) -> float:
@@ -163,6 +172,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--config", default="c1")
     ap.add_argument("--instances", type=int, default=4)
+    ap.add_argument("--kq-heads", type=int, default=0,
+                    help="share q and k among H / N consecutive heads (grouped keys and queries)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="only the warmup and timed decode steps (for counter runs)")
@@ -195,6 +206,9 @@ def main():
             print(msg, file=sys.stderr, flush=True)
 
     cfg = CONFIGS[args.config]
+    if args.kq_heads:
+        import dataclasses
+        cfg = dataclasses.replace(cfg, kq_heads=args.kq_heads)
     W = cfg.W
     NI = args.instances
     wl = Workload(cfg)

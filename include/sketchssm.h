@@ -37,7 +37,8 @@
  *     status is returned; nothing throws across this boundary;
  *   - all arrays are dense row-major with the layouts written beside them.
  * Supported shapes: K = 128, W = 16, V in {64, 80, 128}, 1 <= H <= 256,
- * rank_cap <= 64.
+ * rank_cap <= 64.  Below, Hk = kq_heads (or H when 0) and head h uses key/query
+ * head h / (H / Hk).
  */
 #ifndef SKETCHSSM_H
 #define SKETCHSSM_H
@@ -81,6 +82,9 @@ typedef struct {
     int32_t rank_cap;   /* largest allowed rank (49 on the Nano card; <= 64) */
     int32_t kind;       /* sketchssm_kind */
     int32_t qkv;        /* sketchssm_dtype */
+    int32_t kq_heads;   /* heads of q and k: each is shared by H / kq_heads consecutive
+                           state heads (grouped keys and queries, as a Mamba-2 layer's
+                           B and C are per group); 0 or H = one per head.  Must divide H. */
 } sketchssm_shape;
 
 typedef struct sketchssm_plan sketchssm_plan;   /* opaque, immutable once made */
@@ -132,12 +136,13 @@ size_t sketchssm_frame_elems(const sketchssm_plan* plan);
  *          unchanged and only writes Z (the initial sketch after prefill).
  *   Z      device [sketchssm_z_elems] fp32, out; may be NULL when no head has a rank
  *   basis  device [G, basis_rows, K] fp32
- *   kbuf   device [W,H,B,K] of the qkv dtype      (window keys)
+ *   kbuf   device [W,Hk,B,K] of the qkv dtype     (window keys)
  *   vbuf   device [W,H,B,V] of the qkv dtype      (window values)
  *   abuf   device [W,H,B] fp32 (Mamba-2, GDN) or [W,H,B,K] fp32 (KDA) (decays)
  *   bbuf   device [W,H,B] fp32 (GDN, KDA); must be NULL for Mamba-2
  *          The window is slot-major: slot i of item (b, h) is element
- *          (i*H + h)*B + b.  A decode step then appends one contiguous slab and
+ *          (i*H + h)*B + b of vbuf, abuf, bbuf and (i*Hk + h/(H/Hk))*B + b of
+ *          kbuf; a shared key slot is written once, by the first of its heads.  A decode step then appends one contiguous slab and
  *          reads older slots as contiguous runs of batch rows.
  *   n_tokens 0 .. W
  * The window is not modified; the next window simply starts again at slot 0.
@@ -159,7 +164,7 @@ sketchssm_status sketchssm_flush(const sketchssm_plan* plan, float* S, float* Z,
  *   S       device [B,H,K,V] fp32 state at the last flush (read by dense heads only)
  *   Z       device sketch (see sketchssm_z_elems); may be NULL without sketch heads
  *   frames  device [sketchssm_frame_elems] fp32; may be NULL without sketch heads
- *   q, k    device [B,H,K] qkv dtype
+ *   q, k    device [B,Hk,K] qkv dtype
  *   v       device [B,H,V] qkv dtype
  *   a       device [B,H] fp32 (Mamba-2, GDN) or [B,H,K] fp32 (KDA)
  *   beta    device [B,H] fp32 (GDN, KDA); NULL for Mamba-2
@@ -230,7 +235,7 @@ sketchssm_status sketchssm_dense_read(const sketchssm_shape* shape, const float*
  * every (b, h): S <- M S + beta k v^T, then y = S^T q (the updated state).
  * No window, plan, sketch or basis is involved.
  *   S       device [B,H,K,V] fp32, in/out
- *   q, k    device [B,H,K] qkv dtype;  v device [B,H,V] qkv dtype
+ *   q, k    device [B,Hk,K] qkv dtype;  v device [B,H,V] qkv dtype
  *   a       device [B,H] fp32 (Mamba-2, GDN) or [B,H,K] fp32 (KDA)
  *   beta    device [B,H] fp32 (GDN, KDA); NULL for Mamba-2
  *   y       device [B,H,V] fp32, out

@@ -278,13 +278,20 @@ def items_oracle(wl, items: Sequence[tuple], S_init: Optional[np.ndarray] = None
 
 
 def gather_items(step: dict, items: Sequence[tuple]) -> dict:
-    """Pick the (b, h) items out of full-batch step inputs."""
+    """Pick the (b, h) items out of full-batch step inputs.  When q and k have
+    fewer heads than v, head h uses key/query head h // (H / Hk)."""
     bi = np.array([b for b, _ in items])
     hi = np.array([h for _, h in items])
+    H = step["v"].shape[1]
     out = {}
     for key in ("q", "k", "v", "a", "beta"):
         x = step.get(key)
-        out[key] = None if x is None else x[bi, hi]
+        if x is None:
+            out[key] = None
+        elif key in ("q", "k") and x.shape[1] != H:
+            out[key] = x[bi, hi // (H // x.shape[1])]
+        else:
+            out[key] = x[bi, hi]
     return out
 
 

@@ -35,7 +35,7 @@ class SketchSSMError(RuntimeError):
 class Shape(ctypes.Structure):
     _fields_ = [("B", c_i32), ("H", c_i32), ("K", c_i32), ("V", c_i32), ("W", c_i32),
                 ("G", c_i32), ("basis_rows", c_i32), ("rank_cap", c_i32), ("kind", c_i32),
-                ("qkv", c_i32)]
+                ("qkv", c_i32), ("kq_heads", c_i32)]
 
 
 _lib = None
@@ -80,10 +80,10 @@ def _check(where: str, st: int):
         raise SketchSSMError(where, st)
 
 
-def make_shape(B, H, K, V, W, G, basis_rows, rank_cap, kind, qkv) -> Shape:
+def make_shape(B, H, K, V, W, G, basis_rows, rank_cap, kind, qkv, kq_heads=0) -> Shape:
     return Shape(int(B), int(H), int(K), int(V), int(W), int(G), int(basis_rows), int(rank_cap),
                  KIND[kind] if isinstance(kind, str) else int(kind),
-                 DTYPE[qkv] if isinstance(qkv, str) else int(qkv))
+                 DTYPE[qkv] if isinstance(qkv, str) else int(qkv), int(kq_heads or 0))
 
 
 def _ptr(x) -> Optional[int]:

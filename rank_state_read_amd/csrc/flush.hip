@@ -54,6 +54,7 @@ struct FlushArgs {
     const int32_t* seqs;  // batch rows to flush (continuous batching) or null: every row
     const int32_t* ntok;  // tokens held back per listed row
     int B, H, n_tokens, basis_rows;
+    int Hk, share;  // key heads; each serves `share` consecutive heads
     int nb;   // blocks per head: B, or the number of listed rows
     int omt;  // 16-row tiles of the largest rank
 };
@@ -142,8 +143,9 @@ void flush_kernel(FlushArgs A, HeadTable T) {
     const size_t item = size_t(b) * A.H + h;
     const bool sketch = r > 0 && A.Z != nullptr;
     const int v0 = 16 * w;
-    // window slot i of this item: [W][H][B] layout, slot-major
+    // window slot i of this item: [W][H][B] layout, slot-major (keys: [W][Hk][B])
     auto wslot = [&](int i) { return (size_t(i) * A.H + h) * A.B + b; };
+    auto wslotk = [&](int i) { return (size_t(i) * A.Hk + h / A.share) * A.B + b; };
 
     // ---- 1. window loads into registers, issued first ----
     // Every slot is fetched (the window always holds W slots) and slots >= n
@@ -165,7 +167,7 @@ void flush_kernel(FlushArgs A, HeadTable T) {
     if (n > 0) {
         if (!KDA) as_l = A.abuf[wslot(lane & 15)];
         if (DELTA) bs_l = A.bbuf[wslot(lane & 15)];
-        if (tid < KCH) kraw = V8::load(A.kbuf, wslot(ki) * K + kc0);
+        if (tid < KCH) kraw = V8::load(A.kbuf, wslotk(ki) * K + kc0);
         if (tid < VCH) vraw = V8::load(A.vbuf, wslot(vi) * V + vc0);
         if (KDA) {
 #pragma unroll
@@ -521,6 +523,8 @@ static sketchssm_status run_flush(const sketchssm_plan* plan, float* S, float* Z
     A.n_tokens = listed ? 0 : n_tokens;
     A.basis_rows = sh.basis_rows;
     A.nb = listed ? n_seqs : sh.B;
+    A.Hk = kq_heads_of(sh);
+    A.share = sh.H / A.Hk;
     A.omt = n_sketch > 0 ? (plan->max_rank + 15) / 16 : 0;
     const long grid = long(A.nb) * sh.H;
     if (grid > 0x7fffffffL) return SKSSM_ESHAPE;

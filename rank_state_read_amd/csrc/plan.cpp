@@ -29,6 +29,8 @@ sketchssm_status check_shape(const sketchssm_shape* s) {
     if (s->V != 64 && s->V != 80 && s->V != 128) return SKSSM_ESHAPE;
     if (s->G < 1 || s->G > kMaxHeads) return SKSSM_ESHAPE;
     if (s->basis_rows < 1 || s->rank_cap < 1 || s->rank_cap > kMaxRank) return SKSSM_ESHAPE;
+    if (s->kq_heads < 0 || s->kq_heads > s->H || (s->kq_heads > 0 && s->H % s->kq_heads != 0))
+        return SKSSM_ESHAPE;
     // every index used by the kernels stays below 2^31 elements per array
     const double sz = double(s->B) * s->H * s->K * s->V;
     if (sz >= 2147483648.0) return SKSSM_ESHAPE;

@@ -53,6 +53,7 @@ struct ReadArgs {
     float* y;
     const int32_t* pos_seq;  // per-sequence window positions (continuous batching) or null
     int B, H, pos;
+    int Hk, share;     // key/query heads; each serves `share` consecutive heads
     int n_dense;       // dense heads lead the order
     int tiles;         // ceil(B / 16) blocks per sketch head
     int dense_blocks;  // n_dense * B
@@ -120,7 +121,11 @@ struct RowSweep {
         typename V8::raw_t vc = V8::zero();
         if (l < V / 8) vc = V8::load(stg + kStageV, 8 * l);
         const size_t slot = (size_t(pos) * A.H + h) * A.B + b;
-        V8::store(A.kbuf, slot * kK + 8 * l, kc);
+        // a shared key slot is written once, by the first head of its group
+        if (h % A.share == 0) {
+            const size_t kslot = (size_t(pos) * A.Hk + h / A.share) * A.B + b;
+            V8::store(A.kbuf, kslot * kK + 8 * l, kc);
+        }
         if (l < V / 8) V8::store(A.vbuf, slot * V + 8 * l, vc);
         if (KDA) {
             float ac[8];
@@ -138,15 +143,18 @@ struct RowSweep {
                                                typename V8::raw_t& qr, float (&u)[8],
                                                float (&acc)[8], float& gtot, char* stg) {
         const size_t item = size_t(b) * A.H + h;
-        // window slot i of this item: [W][H][B] layout, slot-major
+        const int kh = h / A.share;                  // key/query head
+        const size_t itemk = size_t(b) * A.Hk + kh;
+        // window slot i of this item: [W][H][B] layout, slot-major (keys: [W][Hk][B])
         auto wslot = [&](int i) { return (size_t(i) * A.H + h) * A.B + b; };
+        auto wslotk = [&](int i) { return (size_t(i) * A.Hk + kh) * A.B + b; };
         const bool vl = l < V / 8;
         // lanes >= V/8 own no value elements; they re-read lane 0's chunk (in
         // bounds, never stored) so that no load sits in a divergent branch,
         // which would make the compiler wait for it at the branch's end
         const int vo = vl ? 8 * l : 0;
-        qr = V8::load(A.q, item * kK + 8 * l);
-        const typename V8::raw_t kc = V8::load(A.k, item * kK + 8 * l);
+        qr = V8::load(A.q, itemk * kK + 8 * l);
+        const typename V8::raw_t kc = V8::load(A.k, itemk * kK + 8 * l);
         const typename V8::raw_t vc = V8::load(A.v, item * V + vo);
         float ac[NA];
         if (KDA) load8f(A.a + item * kK + 8 * l, ac);
@@ -198,7 +206,7 @@ struct RowSweep {
                 bw[j] = 0.f;
                 if (i >= 0) {
                     const size_t si = wslot(i);
-                    kw[j] = V8::load(A.kbuf, si * kK + 8 * l);
+                    kw[j] = V8::load(A.kbuf, wslotk(i) * kK + 8 * l);
                     if (vl) vw[j] = V8::load(A.vbuf, si * V + 8 * l);
                     if (KDA) load8f(A.abuf + si * kK + 8 * l, aw[j]);
                     else aw[j][0] = A.abuf[si];
@@ -549,6 +557,8 @@ static sketchssm_status run_read(const sketchssm_shape& sh, const HeadTable& t, 
     A.H = sh.H;
     A.pos = pos;
     A.pos_seq = pos_seq;
+    A.Hk = kq_heads_of(sh);
+    A.share = sh.H / A.Hk;
     A.n_dense = n_dense;
     A.tiles = (sh.B + kRows - 1) / kRows;
     A.dense_blocks = n_dense * sh.B;

@@ -30,6 +30,7 @@ struct RmwArgs {
     const float* a;
     const float* beta;
     float* y;
+    int Hk, share;  // key/query heads; each serves `share` consecutive heads
 };
 
 template <typename QT>
@@ -66,11 +67,13 @@ void rmw_kernel(RmwArgs A) {
     const int lq = lane >> 4;
     const int v0 = 16 * w;
     const size_t item = blockIdx.x;
+    const size_t h = item % (size_t(A.Hk) * A.share);
+    const size_t itemk = (item / (size_t(A.Hk) * A.share)) * A.Hk + h / A.share;  // (b, key head)
 
     // the token: q, k (and KDA decays) to LDS as fp32; this lane's value
     if (tid < K) {
-        qs[tid] = rmw_load1<QT>(A.q, item * K + tid);
-        ks[tid] = rmw_load1<QT>(A.k, item * K + tid);
+        qs[tid] = rmw_load1<QT>(A.q, itemk * K + tid);
+        ks[tid] = rmw_load1<QT>(A.k, itemk * K + tid);
         if (KDA) als[tid] = A.a[item * K + tid];
     }
     const float a_s = KDA ? 1.f : A.a[item];
@@ -181,6 +184,8 @@ extern "C" sketchssm_status sketchssm_rmw_step(const sketchssm_shape* shape, flo
     A.a = a;
     A.beta = beta;
     A.y = y;
+    A.Hk = kq_heads_of(*shape);
+    A.share = shape->H / A.Hk;
     const long grid = long(shape->B) * shape->H;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = shape->qkv == SKSSM_BF16

@@ -31,6 +31,9 @@ void dense_table(const sketchssm_shape& s, HeadTable* t);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// key/query heads of a (checked) shape: kq_heads, or H when it is 0
+inline int kq_heads_of(const sketchssm_shape& s) { return s.kq_heads > 0 ? s.kq_heads : s.H; }
+
 }  // namespace skssm
 
 struct sketchssm_plan {

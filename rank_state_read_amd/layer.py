@@ -38,11 +38,12 @@ class SketchLayer:
 
     def __init__(self, *, B: int, H: int, K: int, V: int, W: int, G: int, basis_rows: int,
                  rank_cap: int, kind: str, qkv: str, rank, group, basis,
-                 fmap: Optional[Callable] = None, S_init=None, device="cuda"):
+                 fmap: Optional[Callable] = None, S_init=None, device="cuda", kq_heads: int = 0):
         self.kind, self.qkv = kind, qkv
         self.B, self.H, self.K, self.V, self.W = B, H, K, V, W
+        self.Hk = int(kq_heads) if kq_heads else H
         self.device = torch.device(device)
-        self.shape = _shape(B, H, K, V, W, G, basis_rows, rank_cap, kind, qkv)
+        self.shape = _shape(B, H, K, V, W, G, basis_rows, rank_cap, kind, qkv, kq_heads)
         self.plan = _plan(self.shape, rank, group)
         self.layout = self.plan.export()
         dev = self.device
@@ -62,9 +63,10 @@ class SketchLayer:
             self.frames = _to_device(packed, torch.float32, dev)
         qdt = torch.bfloat16 if qkv == "bf16" else torch.float32
         self.qdtype = qdt
-        # the window: slot-major [W][H][B][...], so one decode step appends
-        # one contiguous slab and a block's batch rows are adjacent
-        self.kbuf = torch.zeros((W, H, B, K), dtype=qdt, device=dev)
+        # the window: slot-major [W][H][B][...] (keys [W][Hk][B][K]), so one
+        # decode step appends one contiguous slab and a block's batch rows are
+        # adjacent
+        self.kbuf = torch.zeros((W, self.Hk, B, K), dtype=qdt, device=dev)
         self.vbuf = torch.zeros((W, H, B, V), dtype=qdt, device=dev)
         self.abuf = torch.zeros((W, H, B, K) if kind == "kda" else (W, H, B), dtype=torch.float32, device=dev)
         self.bbuf = torch.zeros((W, H, B), dtype=torch.float32, device=dev) if kind != "mamba2" else None
@@ -133,8 +135,8 @@ class SketchLayer:
         return [self.z_item(b, h) for (b, h) in items]
 
 
-def _shape(B_, H, K, V, W, G, basis_rows, rank_cap, kind, qkv):
-    return _b.make_shape(B_, H, K, V, W, G, basis_rows, rank_cap, kind, qkv)
+def _shape(B_, H, K, V, W, G, basis_rows, rank_cap, kind, qkv, kq_heads=0):
+    return _b.make_shape(B_, H, K, V, W, G, basis_rows, rank_cap, kind, qkv, kq_heads)
 
 
 def _plan(shape, rank, group):
@@ -147,7 +149,8 @@ def layer_for_workload(wl, *, ranks=None, device="cuda", S_init=None, with_state
     rk = wl.ranks if ranks is None else np.asarray(ranks, np.int32)
     lay = SketchLayer(B=c.B, H=c.H, K=c.K, V=c.V, W=c.W, G=c.G, basis_rows=c.basis_rows,
                       rank_cap=c.rank_cap, kind=c.kind, qkv=c.qkv, rank=rk, group=wl.groups,
-                      basis=wl.basis, fmap=wl.fmap, S_init=None, device=device)
+                      basis=wl.basis, fmap=wl.fmap, S_init=None, device=device,
+                      kq_heads=c.kq_heads or 0)
     if S_init is not None:
         lay.S.copy_(_to_device(S_init, torch.float32, lay.device))
     elif with_state:

@@ -30,8 +30,8 @@ def test_library_exports_every_declared_symbol():
     assert set(syms) == set(B._PROTOS)
 
 
-def _shape(H=8, G=2, B_=4, V=80, kind="mamba2", qkv="bf16", cap=49, rows=79):
-    return B.make_shape(B_, H, 128, V, 16, G, rows, cap, kind, qkv)
+def _shape(H=8, G=2, B_=4, V=80, kind="mamba2", qkv="bf16", cap=49, rows=79, kq=0):
+    return B.make_shape(B_, H, 128, V, 16, G, rows, cap, kind, qkv, kq)
 
 
 def test_plan_matches_oracle_rule_bit_exact():
@@ -68,6 +68,7 @@ def test_plan_hand_example_from_library(golden_dir):
 
 @pytest.mark.parametrize("bad", [
     dict(H=0), dict(H=257), dict(V=96), dict(G=0), dict(cap=65), dict(B_=0),
+    dict(kq=3), dict(kq=16), dict(kq=-1),
 ])
 def test_plan_rejects_bad_shapes(bad):
     kw = dict(H=8, G=2)
@@ -182,6 +183,11 @@ def test_seq_entry_points_argument_errors():
     assert L.sketchssm_flush_seq(h, *(fl[:3] + [None] + fl[4:]), FAKE, FAKE, 1, None) == 1  # window needed
     assert L.sketchssm_flush_seq(h, *fl, FAKE, FAKE, 0, None) == 0     # empty list: nothing to do
     assert L.sketchssm_flush_seq(h, *fl, FAKE + 2, FAKE, 1, None) == 3
+
+
+def test_shared_key_heads_accepted():
+    for kq in (0, 1, 2, 4, 8):
+        B.Plan(_shape(kq=kq), np.full(8, 3, np.int32), np.repeat(np.arange(2, dtype=np.int32), 4))
 
 
 def test_status_strings():

@@ -143,6 +143,26 @@ def test_reduced_batch_all_items(name, B, steps):
 
 
 @pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,kq,B,steps", [("c1", 8, 20, 40), ("c3", 8, 19, 36), ("c4", 16, 19, 36),
+                                             ("c0", 2, 2, 40)])
+def test_shared_key_heads(name, kq, B, steps):
+    """q, k and the window's keys shared by H / kq consecutive heads."""
+    import dataclasses
+    cfg = dataclasses.replace(CONFIGS[name].with_batch(B), kq_heads=kq)
+    _run_steps(Workload(cfg), steps)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,kq", [("c1", 8), ("c4", 16)])
+def test_shared_key_heads_dense_baseline(name, kq):
+    import dataclasses
+    cfg = dataclasses.replace(CONFIGS[name].with_batch(19), kq_heads=kq)
+    wl = Workload(cfg)
+    wl0 = Workload(cfg, ranks=np.zeros(cfg.H, np.int32), basis=wl.basis)
+    _run_steps(wl0, cfg.W + 5, dense_baseline=True, step_source=wl)
+
+
+@pytest.mark.timeout(300)
 @pytest.mark.parametrize("name", ["c1", "c3", "c4"])
 def test_long_run_drift(name):
     """Many windows on a few items: errors must not grow with the flush count."""

@@ -70,6 +70,13 @@ def test_rmw_matches_exact_recurrence(name, B, steps):
     _run(Workload(CONFIGS[name].with_batch(B)), steps)
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,kq", [("c1", 8), ("c3", 8), ("c4", 16)])
+def test_rmw_shared_key_heads(name, kq):
+    import dataclasses
+    _run(Workload(dataclasses.replace(CONFIGS[name].with_batch(19), kq_heads=kq)), 20)
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["c1", "c4"])
 def test_rmw_full_size_sampled(name):

@@ -49,9 +49,10 @@ def _schedule(B, T, W, seed):
     return join, idle, early
 
 
-def _run(name, B, T):
+def _run(name, B, T, kq=None):
+    import dataclasses
     from rank_state_read_amd.layer import layer_for_workload
-    cfg = CONFIGS[name].with_batch(B)
+    cfg = dataclasses.replace(CONFIGS[name].with_batch(B), kq_heads=kq)
     wl = Workload(cfg)
     W, H = cfg.W, cfg.H
     lay = layer_for_workload(wl)
@@ -128,6 +129,7 @@ def _run(name, B, T):
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("name,B", [("c1", 20), ("c1", 37), ("c3", 19), ("c4", 19), ("c0", 2)])
-def test_staggered_windows(name, B):
-    _run(name, B, 2 * CONFIGS[name].W + 9)
+@pytest.mark.parametrize("name,B,kq", [("c1", 20, None), ("c1", 37, 8), ("c3", 19, None), ("c4", 19, 16),
+                                       ("c0", 2, None)])
+def test_staggered_windows(name, B, kq):
+    _run(name, B, 2 * CONFIGS[name].W + 9, kq)

@@ -101,3 +101,21 @@ def test_nano_layer_matches_calibration_card(golden_dir):
     assert CONFIGS["c2"].n_dense == round(tab[21]["dense"] / total * 128)
     assert abs(tab[6]["dense"] / total - 0.01) < 0.002 and CONFIGS["c1"].n_dense == 1
     assert abs(tab[10]["dense"] / total - 0.07) < 0.01
+
+
+def test_shared_keys_gather_to_their_heads():
+    """With keys and queries shared by groups of heads, the oracle's per-item
+    gather picks each head's key/query head and matches the single-item draw."""
+    import dataclasses
+    from oracle import gather_items
+    cfg = dataclasses.replace(CONFIGS["c1"].with_batch(3), kq_heads=8)
+    wl = Workload(cfg)
+    st = wl.step(4)
+    assert st["q"].shape == (3, 8, 128) and st["k"].shape == (3, 8, 128) and st["v"].shape == (3, 128, 80)
+    items = [(0, 0), (1, 15), (1, 16), (2, 127), (2, 64)]
+    g = gather_items(st, items)
+    for i, (b, h) in enumerate(items):
+        one = wl.step_item(4, b, h)
+        for key in ("q", "k", "v", "a"):
+            assert np.array_equal(g[key][i], one[key]), (key, b, h)
+        assert np.array_equal(g["k"][i], st["k"][b, h // 16])

@@ -65,6 +65,7 @@ class Config:
     seed: int
     basis_rows: int = 79
     fixed_rank: Optional[int] = None  # every sketch head gets this rank
+    kq_heads: Optional[int] = None  # q/k heads, each shared by H / kq_heads heads (None: one per head)
     query_noise: float = 0.05
     state_std: float = 0.02
     decay_scale: float = 0.1
@@ -78,6 +79,11 @@ class Config:
     @property
     def heads_per_group(self) -> int:
         return self.H // self.G
+
+    @property
+    def Hk(self) -> int:
+        """Key/query heads (H unless keys and queries are shared)."""
+        return self.kq_heads or self.H
 
     @property
     def per_channel_decay(self) -> bool:
@@ -258,6 +264,7 @@ class Workload:
                  basis: Optional[np.ndarray] = None):
         assert cfg.kind in KINDS
         assert cfg.H % cfg.G == 0
+        assert cfg.H % cfg.Hk == 0
         self.cfg = cfg
         self.basis = make_basis(cfg) if basis is None else np.asarray(basis, dtype=np.float32)
         self.ranks = make_ranks(cfg) if ranks is None else np.asarray(ranks, dtype=np.int32)
@@ -305,37 +312,43 @@ class Workload:
         return bf16_bits_to_f32(bits), bits
 
     def _tokens(self, t: int, b0: int, b1: int, heads: np.ndarray) -> dict:
-        """Inputs of step t for batch rows b0..b1-1 and the given heads."""
+        """Inputs of step t for batch rows b0..b1-1 and the given heads.  q and k
+        are per key/query head: for the key heads of the given heads, in order."""
         c = self.cfg
         R = c.rank_cap
         nb = b1 - b0
-        nh = len(heads)
+        Hk = c.Hk
+        share = c.H // Hk
+        kheads = np.unique(np.asarray(heads) // share)
 
-        def draw(stream, width):
-            out = np.empty((nb, nh, width), dtype=np.float64)
-            if nh == c.H and np.array_equal(heads, np.arange(c.H)):
-                out[:] = normals(c.seed, stream, t, b0 * c.H * width, nb * c.H * width).reshape(nb, c.H, width)
+        def draw(stream, width, total, idx):
+            out = np.empty((nb, len(idx), width), dtype=np.float64)
+            if len(idx) == total and np.array_equal(idx, np.arange(total)):
+                out[:] = normals(c.seed, stream, t, b0 * total * width, nb * total * width).reshape(nb, total, width)
                 return out
             for bi in range(nb):
-                for hi, h in enumerate(heads):
-                    out[bi, hi] = normals(c.seed, stream, t, ((b0 + bi) * c.H + int(h)) * width, width)
+                for j, h in enumerate(idx):
+                    out[bi, j] = normals(c.seed, stream, t, ((b0 + bi) * total + int(h)) * width, width)
             return out
 
-        u = draw(_ST_U, R)
-        n = draw(_ST_N, c.K)
-        kk = draw(_ST_K, c.K)
-        vv = draw(_ST_V, c.V)
-        dx = draw(_ST_DECAY, c.K if c.per_channel_decay else 1)
-        bx = draw(_ST_BETA, 1) if c.has_beta else None
+        u = draw(_ST_U, R, Hk, kheads)
+        n = draw(_ST_N, c.K, Hk, kheads)
+        kk = draw(_ST_K, c.K, Hk, kheads)
+        vv = draw(_ST_V, c.V, c.H, heads)
+        dx = draw(_ST_DECAY, c.K if c.per_channel_decay else 1, c.H, heads)
+        bx = draw(_ST_BETA, 1, c.H, heads) if c.has_beta else None
 
-        q = np.empty((nb, nh, c.K), dtype=np.float64)
-        for hi, h in enumerate(heads):
-            r = int(self.ranks[h])
-            if r == 0:
-                q[:, hi, :] = n[:, hi, :]
+        # a query lies near the span of the basis rows its heads read: with a
+        # shared query, the largest rank among the sketch heads that share it
+        q = np.empty((nb, len(kheads), c.K), dtype=np.float64)
+        for j, kh in enumerate(kheads):
+            members = [h for h in range(int(kh) * share, (int(kh) + 1) * share) if self.ranks[h] > 0]
+            if not members:
+                q[:, j, :] = n[:, j, :]
             else:
-                om = self.basis[int(self.groups[h]), :r, :].astype(np.float64)
-                q[:, hi, :] = u[:, hi, :r] @ om + c.query_noise * n[:, hi, :]
+                r = max(int(self.ranks[h]) for h in members)
+                om = self.basis[int(self.groups[members[0]]), :r, :].astype(np.float64)
+                q[:, j, :] = u[:, j, :r] @ om + c.query_noise * n[:, j, :]
         kk = kk / np.linalg.norm(kk, axis=-1, keepdims=True)
         a = np.exp(-_softplus(dx) * c.decay_scale)
         if not c.per_channel_decay:
@@ -349,7 +362,7 @@ class Workload:
         return out
 
     def step(self, t: int) -> dict:
-        """Inputs of step t for the whole batch: arrays [B, H, ...]."""
+        """Inputs of step t for the whole batch: arrays [B, H, ...] (q, k: [B, Hk, K])."""
         return self._tokens(t, 0, self.cfg.B, np.arange(self.cfg.H))
 
     def step_item(self, t: int, b: int, h: int) -> dict:
@@ -361,4 +374,4 @@ class Workload:
 def describe(cfg: Config) -> str:
     return (f"{cfg.name}: {cfg.kind} B={cfg.B} H={cfg.H} K={cfg.K} V={cfg.V} G={cfg.G} "
             f"W={cfg.W} steps={cfg.steps} qkv={cfg.qkv} mean_rank={cfg.mean_rank} "
-            f"dense={cfg.n_dense}")
+            f"dense={cfg.n_dense}" + (f" kq_heads={cfg.kq_heads}" if cfg.kq_heads else ""))
