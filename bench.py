@@ -171,7 +171,12 @@ def main():
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--config", default="c1")
-    ap.add_argument("--instances", type=int, default=4)
+    ap.add_argument("--instances", type=int, default=4,
+                    help="independent layer instances the steps rotate over")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="model decode loop over N recurrent layers (sets --instances N; e.g. 27 for the Nano model)")
+    ap.add_argument("--calibration", default=None,
+                    help="calibration file whose per-layer basis replaces the synthetic one (layer i uses basis i)")
     ap.add_argument("--kq-heads", type=int, default=0,
                     help="share q and k among H / N consecutive heads (grouped keys and queries)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -210,17 +215,29 @@ def main():
         import dataclasses
         cfg = dataclasses.replace(cfg, kq_heads=args.kq_heads)
     W = cfg.W
-    NI = args.instances
+    NI = args.layers or args.instances
     wl = Workload(cfg)
+    cal = None
+    if args.calibration:
+        from rank_state_read_amd.calibration import load_calibration
+        cal = load_calibration(args.calibration, K=cfg.K)
+        if cal["groups"] != cfg.G or cal["rows"] < cfg.rank_cap:
+            print(f"calibration basis {cal['omega'].shape} does not fit G={cfg.G}, rank cap {cfg.rank_cap}",
+                  file=sys.stderr)
+            sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
     t0 = time.time()
     lay0 = layer_for_workload(wl, device=dev)
     log(f"state generated ({time.time() - t0:.1f}s)")
+    if cal is not None:
+        lay0 = layer_for_workload(Workload(cfg, ranks=wl.ranks, basis=cal["omega"][0]), device=dev,
+                                  S_init=lay0.S)
     lays = [lay0]
-    for _ in range(NI - 1):
-        lays.append(layer_for_workload(wl, device=dev, S_init=lay0.S))
+    for i in range(1, NI):
+        wli = wl if cal is None else Workload(cfg, ranks=wl.ranks, basis=cal["omega"][i % len(cal["omega"])])
+        lays.append(layer_for_workload(wli, device=dev, S_init=lay0.S))
     host_steps = [wl.step(t) for t in range(W)]
     inputs = [lay0.upload_step(st) for st in host_steps]
     log(f"inputs generated ({time.time() - t0:.1f}s)")
@@ -356,7 +373,8 @@ def main():
         "data": "synthetic",
         "hbm_GBps": round(sb / (us_step * 1e3), 1),
         "config": {"workload": workload_name(cfg, ranks),
-                   "global_batch": cfg.B, "layer_instances": NI, "parallelism": "none (1 GPU)"},
+                   "global_batch": cfg.B, "layer_instances": NI, "parallelism": "none (1 GPU)",
+                   **({"basis": f"calibration file, layers {cal['layer_ids'][:NI]}"} if cal is not None else {})},
         "roofline": {"bound": "hbm", "kernel": "read_kernel (sketchssm_decode_read)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(cfg.name),
@@ -378,6 +396,7 @@ def main():
             "dense_flush_us": round(dense_flush_us, 2),
             "read_ratio_dense_over_sketch": round(dense_read_us / read_us, 3),
             "layer_ratio_dense_over_sketch": round(dense_step_us / us_step, 3),
+            "model_token_us_all_layers": round(us_step * NI, 2) if args.layers else None,
             "continuous_batching_step_us": round(seq_step_us, 3),
             "rmw_step_us": round(rmw_us, 2),
             "rmw_GBps": round(rmw_bytes(cfg) / (rmw_us * 1e3), 1),
