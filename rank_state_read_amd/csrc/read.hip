@@ -243,6 +243,7 @@ struct RowSweep {
 // ---------------------------------------------------------------------------
 constexpr int kRows = kReadThreads / 16;
 constexpr int kMapRows = 16;  // coefficient-map rows staged in LDS at a time
+static_assert(kK == 128, "the map granule order is laid out for 32 granules per row");
 
 template <int KIND, int V, typename QT, bool SEQ>
 __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable& T, int sb,
@@ -277,13 +278,21 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
 
     // the coefficient map straight into LDS, kMapRows rows at a time (wave w
     // fills 1 KB pieces w, w+4, ...); most heads need a single piece, and the
-    // block's LDS stays small enough for eight resident blocks per CU
+    // block's LDS stays small enough for eight resident blocks per CU.  Inside
+    // a map row the 16-byte granules are stored as 0, 2, .., 30, 1, 3, .., 31:
+    // lane l reads its key elements 8l .. 8l+7 as granules l and 16 + l, so
+    // each of its two reads covers 256 contiguous bytes across the 16 lanes
+    // (every bank once).  A piece with an odd row count also fills the slots
+    // of one row more (the launcher sizes the map for an even row count).
     auto stage_map = [&](int m0) {
         const float4* fsrc = reinterpret_cast<const float4*>(A.frames + (frow + m0) * K);
         const int n4 = min(kMapRows, r - m0) * (K / 4);
         const int w = tid >> 6, L = tid & 63;
         for (int c = w; c * 64 < n4; c += kReadThreads / 64) {
-            const int e = min(c * 64 + L, n4 - 1);
+            const int d = c * 64 + L;  // the LDS granule this lane fills
+            const int sl = d & (K / 4 - 1);
+            const int g = (d & ~(K / 4 - 1)) | (sl < K / 8 ? 2 * sl : 2 * (sl - K / 8) + 1);
+            const int e = min(g, n4 - 1);
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(fsrc + e),
                                              (__attribute__((address_space(3))) void*)(lds4 + kMapOff4 + c * 64),
                                              16, 0, 0);
@@ -337,7 +346,10 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
             {
                 float f[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) f[e] = fmap_s[(m - m0) * K + 8 * l + e];
+                for (int e = 0; e < 4; ++e) {
+                    f[e] = fmap_s[(m - m0) * K + 4 * l + e];
+                    f[4 + e] = fmap_s[(m - m0) * K + K / 2 + 4 * l + e];
+                }
                 const float c0 = row_sum16(dot8(f, u));
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[e] = fmaf(c0, z0[e], acc[e]);
@@ -345,7 +357,10 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
             if (m + 1 < mend) {
                 float f[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) f[e] = fmap_s[(m + 1 - m0) * K + 8 * l + e];
+                for (int e = 0; e < 4; ++e) {
+                    f[e] = fmap_s[(m + 1 - m0) * K + 4 * l + e];
+                    f[4 + e] = fmap_s[(m + 1 - m0) * K + K / 2 + 4 * l + e];
+                }
                 const float c1 = row_sum16(dot8(f, u));
 #pragma unroll
                 for (int e = 0; e < 8; ++e) acc[e] = fmaf(c1, z1[e], acc[e]);
@@ -568,7 +583,10 @@ static sketchssm_status run_read(const sketchssm_shape& sh, const HeadTable& t, 
     const size_t eb = sh.qkv == SKSSM_BF16 ? 2 : 4;
     const size_t stage = kK * eb + size_t(sh.V) * eb + (sh.kind == SKSSM_KDA ? kK * 4 : 0) + 16;
     size_t lds = 0;
-    if (n_sketch > 0) lds = kRows * stage + size_t(max_rank < kMapRows ? max_rank : kMapRows) * kK * sizeof(float);
+    // the map piece: min(max_rank, kMapRows) rows, rounded up to even (the
+    // staging fills whole 64-granule chunks)
+    const int map_rows = ((max_rank < kMapRows ? max_rank : kMapRows) + 1) & ~1;
+    if (n_sketch > 0) lds = kRows * stage + size_t(map_rows) * kK * sizeof(float);
     if (n_dense > 0) {
         const size_t dl = (sh.V == 64 ? DenseLds<64>::bytes : sh.V == 80 ? DenseLds<80>::bytes : DenseLds<128>::bytes) + stage;
         lds = lds > dl ? lds : dl;
