@@ -142,8 +142,9 @@ size_t sketchssm_frame_elems(const sketchssm_plan* plan);
  *   bbuf   device [W,H,B] fp32 (GDN, KDA); must be NULL for Mamba-2
  *          The window is slot-major: slot i of item (b, h) is element
  *          (i*H + h)*B + b of vbuf, abuf, bbuf and (i*Hk + h/(H/Hk))*B + b of
- *          kbuf; a shared key slot is written once, by the first of its heads.  A decode step then appends one contiguous slab and
- *          reads older slots as contiguous runs of batch rows.
+ *          kbuf; a shared key slot is written once, by the first of its heads.
+ *          A decode step then appends one contiguous slab and reads older
+ *          slots as contiguous runs of batch rows.
  *   n_tokens 0 .. W
  * The window is not modified; the next window simply starts again at slot 0.
  */

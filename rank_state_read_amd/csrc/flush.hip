@@ -2,11 +2,11 @@
 //
 // One block per (b, h) item; consecutive blocks walk the batch of one head, so
 // the head's basis rows stay in L2.  With a row list (continuous batching)
-// the blocks walk the listed rows instead, each with its own token count.  The block has V/16 waves; wave w owns
-// value columns 16w .. 16w+15 of the item's fp32 state and holds all K = 128
-// key rows of them in registers as eight 16x16 MFMA accumulator tiles
-// (lane l, register r <-> S[16 kt + 4 (l/16) + r][16 w + l%16]).  In one pass
-// over the state it
+// the blocks walk the listed rows instead, each with its own token count.  The
+// block has V/16 waves; wave w owns value columns 16w .. 16w+15 of the item's
+// fp32 state and holds all K = 128 key rows of them in registers as eight
+// 16x16 MFMA accumulator tiles (lane l, register r <-> S[16 kt + 4 (l/16) + r]
+// [16 w + l%16]).  In one pass over the state it
 //   1. applies the window's n held-back tokens (page "SketchSSM: Write to the
 //      Full State, Read from a Compact Sketch", Abstract: keys and values wait
 //      for a periodic exact update; W = 16 on the Nemotron Nano 9B v2
@@ -56,7 +56,7 @@ struct FlushArgs {
     int B, H, n_tokens, basis_rows;
     int Hk, share;  // key heads; each serves `share` consecutive heads
     int nb;   // blocks per head: B, or the number of listed rows
-    int omt;  // 16-row tiles of the largest rank
+    int omt;  // basis tiles held in LDS: 1 when the plan has sketch heads, else 0
 };
 
 // LDS map, in floats.  Row strides are 4 (mod 16) floats: the rows 4 (l/16) + s
@@ -75,7 +75,7 @@ struct FlushLds {
     static constexpr int lt = kg + (delta ? 16 * KS : 0);  // delta: L transposed [16][16]
     static constexpr int tm = lt + (delta ? 256 : 0);      // delta: T [16][16]
     static constexpr int al = tm + (delta ? 256 : 0);      // KDA: decays [16][K]
-    static constexpr int om = al + (kda ? 16 * kK : 0);    // basis rows [16 omt][K], swizzled
+    static constexpr int om = al + (kda ? 16 * kK : 0);    // one tile of basis rows [16][K], swizzled
     static size_t bytes(int omt) { return size_t(om + 16 * omt * kK) * 4; }
 };
 
@@ -178,28 +178,32 @@ void flush_kernel(FlushArgs A, HeadTable T) {
         }
     }
 
-    // ---- 2. basis rows, straight into LDS (16-byte granules; granule c of
-    // row m is stored at slot c ^ (m % 16) so that the sixteen rows one A
-    // operand read touches fall in distinct banks).  Rows from r up to the
-    // next multiple of 16 repeat row r - 1: they only feed sketch rows that
-    // are never stored.
-    if (sketch) {
+    // ---- 2. basis rows, straight into LDS, one 16-row tile at a time (16-byte
+    // granules; granule c of row m is stored at slot c ^ (m % 16) so that the
+    // sixteen rows one A-operand read touches fall in distinct banks).  Rows
+    // from r up to the next multiple of 16 repeat row r - 1: they only feed
+    // sketch rows that are never stored.  Holding one tile instead of the
+    // largest rank's rows keeps the block's LDS small enough that registers,
+    // not LDS, bound the resident blocks (c1: four 320-thread blocks per CU
+    // instead of three).  The first tile is requested here, with the window.
+    auto stage_basis = [&](int mt) {
         const float* om = A.basis + size_t(g) * A.basis_rows * K;
-        const int half_rows = 8 * ((r + 15) >> 4);
 #pragma unroll
-        for (int j = 0; j < (8 * kMaxRank / 16 + NW - 1) / NW; ++j) {
-            const int qd = wu + j * NW;
-            if (qd < half_rows) {
+        for (int j = 0; j < (8 + NW - 1) / NW; ++j) {
+            const int qd = wu + j * NW;  // 64-granule chunk: tile rows 2 qd, 2 qd + 1
+            if (qd < 8) {
                 const int gi = 64 * qd + lane;
                 const int m = gi >> 5;
-                const int c4 = (gi & 31) ^ (m & 15);
-                const int srow = m < r ? m : r - 1;
+                const int c4 = (gi & 31) ^ m;
+                const int row = 16 * mt + m;
+                const int srow = row < r ? row : r - 1;
                 __builtin_amdgcn_global_load_lds(
                     (const __attribute__((address_space(1))) void*)(om + size_t(srow) * K + 4 * c4),
                     (__attribute__((address_space(3))) void*)(Om + 256 * qd), 16, 0, 0);
             }
         }
-    }
+    };
+    if (sketch) stage_basis(0);
 
     // Window and basis rows first, the state after: while direct-to-LDS loads
     // are outstanding the memory counter cannot tell loads apart, so every
@@ -410,7 +414,15 @@ void flush_kernel(FlushArgs A, HeadTable T) {
         float* Zi = A.Z + (size_t(T.zrow[p]) * A.B + size_t(b) * r) * V;
         const int mts = (r + 15) >> 4;
         for (int mt = 0; mt < mts; ++mt) {
-            const float* orow = Om + (16 * mt + lr) * K;
+            if (mt > 0) {
+                // ranks above 16: the next tile replaces the last one (a cache
+                // hit: the head's blocks run back to back)
+                __syncthreads();
+                stage_basis(mt);
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's granules
+                __syncthreads();
+            }
+            const float* orow = Om + lr * K;
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kt = 0; kt < 8; ++kt) {
@@ -525,7 +537,7 @@ static sketchssm_status run_flush(const sketchssm_plan* plan, float* S, float* Z
     A.nb = listed ? n_seqs : sh.B;
     A.Hk = kq_heads_of(sh);
     A.share = sh.H / A.Hk;
-    A.omt = n_sketch > 0 ? (plan->max_rank + 15) / 16 : 0;
+    A.omt = n_sketch > 0 ? 1 : 0;
     const long grid = long(A.nb) * sh.H;
     if (grid > 0x7fffffffL) return SKSSM_ESHAPE;
     hipStream_t s = static_cast<hipStream_t>(stream);

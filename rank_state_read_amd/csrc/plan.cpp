@@ -127,7 +127,6 @@ extern "C" sketchssm_status sketchssm_plan_export(const sketchssm_plan* p, int32
                                                   int32_t* frame_group, int32_t* frame_rank,
                                                   int32_t* n_frames) {
     if (!p) return SKSSM_EINVAL;
-    const int H = p->shape.H;
     auto cp = [](int32_t* dst, const std::vector<int32_t>& src) {
         if (dst && !src.empty()) std::memcpy(dst, src.data(), src.size() * sizeof(int32_t));
     };
@@ -139,7 +138,6 @@ extern "C" sketchssm_status sketchssm_plan_export(const sketchssm_plan* p, int32
     cp(frame_group, p->frame_group);
     cp(frame_rank, p->frame_rank);
     if (n_frames) *n_frames = p->n_frames;
-    (void)H;
     return SKSSM_OK;
 }
 
