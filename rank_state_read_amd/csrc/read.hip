@@ -479,18 +479,21 @@ __device__ __forceinline__ void dense_block(const ReadArgs& A, const HeadTable& 
 }
 
 // Waves per SIMD the register budget is sized for: 8 (64 VGPRs) where the
-// sweep fits, 5 (96 VGPRs) for the wider per-channel / fp32 variants.
-template <int KIND, int V, typename QT>
+// sweep fits, 5 (96 VGPRs) for the wider per-channel / fp32 variants, 4 (128)
+// for the fp32 V = 128 per-sequence instances, which need a little more.
+template <int KIND, int V, typename QT, bool SEQ>
 struct ReadOccupancy {
-    static constexpr int value =
-        (KIND == SKSSM_MAMBA2 && V <= 80 && std::is_same<QT, Bf16Tag>::value) ? 8 : 5;
+    static constexpr bool kF32 = std::is_same<QT, F32Tag>::value;
+    static constexpr int value = (KIND == SKSSM_MAMBA2 && V <= 80 && !kF32) ? 8
+                                 : (SEQ && kF32 && V == 128)               ? 4
+                                                                            : 5;
 };
 
 // SEQ: every sequence has its own window position (continuous batching);
 // otherwise the whole batch is at position A.pos.
 template <int KIND, int V, typename QT, bool SEQ>
 __global__ __launch_bounds__(kReadThreads)
-__attribute__((amdgpu_waves_per_eu(ReadOccupancy<KIND, V, QT>::value)))
+__attribute__((amdgpu_waves_per_eu(ReadOccupancy<KIND, V, QT, SEQ>::value)))
 void read_kernel(ReadArgs A, HeadTable T) {
     extern __shared__ float4 lds4[];  // token staging + coefficient map (sketch) or reduction buffers (dense)
     const int blk = blockIdx.x;
