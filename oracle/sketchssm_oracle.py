@@ -204,6 +204,16 @@ class BatchOracle:
     S_init: [n, K, V].  omega / fmap: per item (r_i x K) arrays or None for a
     dense item.  Sketch quantities are zero-padded to the largest rank, which
     leaves Z^T c unchanged.
+
+    ``traffic`` counts the bytes of stored fp32 state and sketch that the
+    method moves, at the points where this class uses them: a sketch item's
+    output is formed from its r_i x V sketch rows (Z read), a dense item's from
+    the K x V state at the last flush (S read); a flush reads and writes the
+    state once and writes the sketch (the Abstract of "SketchSSM: Write to the
+    Full State, Read from a Compact Sketch": the state is read once per update,
+    decode steps read only the sketch).  The initial sketch reads the state
+    once and writes Z.  Window tokens and query-side data are not state and
+    are not counted.
     """
 
     def __init__(self, kind: str, W: int, S_init: np.ndarray,
@@ -214,6 +224,7 @@ class BatchOracle:
         n, K, V = self.S.shape
         self.n, self.K, self.V = n, K, V
         self.dense = np.array([om is None for om in omega], dtype=bool)
+        self.rank = np.array([0 if om is None else om.shape[0] for om in omega], dtype=np.int64)
         self.R = max([0] + [om.shape[0] for om in omega if om is not None])
         R = max(self.R, 1)
         self.omega = np.zeros((n, R, K))
@@ -223,9 +234,20 @@ class BatchOracle:
                 r = omega[i].shape[0]
                 self.omega[i, :r] = omega[i]
                 self.fmap[i, :r] = fmap[i]
-        self._flush_state()
+        self.traffic = {"S_read": 0, "S_write": 0, "Z_read": 0, "Z_write": 0}
+        self._flush_state(initial=True)
 
-    def _flush_state(self):
+    def _count_flush(self, initial: bool):
+        kv = 4 * self.K * self.V
+        sketch = ~self.dense
+        # the initial sketch only needs the sketch items' states
+        self.traffic["S_read"] += kv * (int(sketch.sum()) if initial else self.n)
+        if not initial:
+            self.traffic["S_write"] += kv * self.n
+        self.traffic["Z_write"] += 4 * self.V * int(self.rank[sketch].sum())
+
+    def _flush_state(self, initial: bool = False):
+        self._count_flush(initial)
         self.S0 = self.S.copy()
         self.Hs = np.zeros_like(self.S)                       # window-only state
         self.Q = np.transpose(self.fmap, (0, 2, 1)).copy()    # P F_r^T, P = I
@@ -250,6 +272,8 @@ class BatchOracle:
         intra = np.einsum("nkv,nk->nv", self.Hs, q)
         y = np.einsum("nrv,nr->nv", self.Z, c) + intra
         y[self.dense] = y_exact[self.dense]
+        self.traffic["Z_read"] += 4 * self.V * int(self.rank[~self.dense].sum())
+        self.traffic["S_read"] += 4 * self.K * self.V * int(self.dense.sum())
         return y, y_exact
 
     def flush(self):

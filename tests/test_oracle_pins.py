@@ -441,3 +441,66 @@ def test_intra_is_the_explicit_sum(kind):
             bi = 1.0 if kind == "mamba2" else toks[i - 1]["beta"]
             want += bi * toks[i - 1]["v"] * (toks[i - 1]["k"] @ u)
         np.testing.assert_allclose(intra_oracle, want, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# state-access traffic
+# ---------------------------------------------------------------------------
+def _traffic_oracle(ranks, K=128, V=80, W=16, seed=9):
+    """A BatchOracle over items of the given ranks (0 = dense), random orthonormal
+    basis rows, run through one full window and its flush."""
+    rng = np.random.default_rng(seed)
+    Om, _ = np.linalg.qr(rng.standard_normal((K, K)))
+    Om = Om.T
+    n = len(ranks)
+    omega = [None if r == 0 else Om[:r] for r in ranks]
+    fmap = [None if r == 0 else Om[:r] for r in ranks]
+    orc = BatchOracle("mamba2", W, 0.02 * rng.standard_normal((n, K, V)), omega, fmap)
+    start = dict(orc.traffic)
+    per_read = []
+    for _ in range(W):
+        before = dict(orc.traffic)
+        k = rng.standard_normal((n, K))
+        orc.read(rng.standard_normal((n, K)), k / np.linalg.norm(k, axis=1, keepdims=True),
+                 rng.standard_normal((n, V)), rng.uniform(0.9, 1.0, n))
+        per_read.append({key: orc.traffic[key] - before[key] for key in before})
+    orc.flush()
+    return orc, start, per_read
+
+
+def test_sketch_read_traffic_is_rank_over_K():
+    """A decode read of a rank-r head moves r/K of the state bytes that a dense
+    (full-state) read moves: Z is r x V, S is K x V."""
+    K, V = 128, 80
+    _, _, de = _traffic_oracle([0], K=K, V=V)
+    for r in (1, 6, 8, 16, 49):
+        _, _, sk = _traffic_oracle([r], K=K, V=V)
+        for a, b in zip(sk, de):
+            assert a["S_read"] == 0 and a["S_write"] == 0 and a["Z_write"] == 0
+            assert b["Z_read"] == 0 and b["S_write"] == 0
+            assert Fraction(a["Z_read"], b["S_read"]) == Fraction(r, K)
+    # heads of mixed ranks in one launch: each moves its own r/K, not the largest
+    ranks = [1, 6, 8, 16, 49, 0, 0]
+    _, _, mixed = _traffic_oracle(ranks, K=K, V=V)
+    for a in mixed:
+        assert Fraction(a["Z_read"], de[0]["S_read"]) == Fraction(sum(ranks), K)
+        assert a["S_read"] == 2 * de[0]["S_read"]
+
+
+def test_state_traffic_about_ten_times_lower_at_mean_rank_8():
+    """The Abstract of "SketchSSM: Write to the Full State, Read from a Compact
+    Sketch" reports about 10x less state-access traffic at a mean sketch rank
+    of 8.  Against the standard decode, which reads and writes the whole state
+    for every token, one window of W = 16 tokens of rank-8 heads (Nano shape,
+    K = 128) moves 2KW / (rW + 2K + r) = 10.45x fewer state bytes."""
+    K, V, W, r, n = 128, 80, 16, 8, 4
+    orc, start, _ = _traffic_oracle([r] * n, K=K, V=V, W=W)
+    moved = sum(orc.traffic[key] - start[key] for key in orc.traffic)
+    standard = W * n * 2 * K * V * 4
+    ratio = standard / moved
+    assert ratio == pytest.approx(2 * K * W / (r * W + 2 * K + r), rel=1e-12)
+    assert 9.5 < ratio < 11.5
+    # dense heads gain nothing: their reads are full state reads
+    orc, start, _ = _traffic_oracle([0] * n, K=K, V=V, W=W)
+    moved = sum(orc.traffic[key] - start[key] for key in orc.traffic)
+    assert standard / moved == pytest.approx(2 * W / (W + 2), rel=1e-12)
