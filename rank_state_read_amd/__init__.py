@@ -13,7 +13,10 @@ from .binding import (  # noqa: F401
     lib,
     make_shape,
     sketchssm_decode_read,
+    sketchssm_decode_read_seq,
     sketchssm_dense_read,
     sketchssm_flush,
+    sketchssm_flush_seq,
+    sketchssm_rmw_step,
     status_string,
 )

@@ -236,6 +236,16 @@ def test_rank_extremes(kind, V):
 
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("kind,V", [("mamba2", 80), ("gdn", 128), ("kda", 128)])
+def test_small_odd_largest_rank(kind, V):
+    """A plan whose largest rank is odd and below 16 (the coefficient map's LDS
+    piece then has an odd row count)."""
+    cfg = _edge_cfg(kind, V)
+    ranks = np.array([1, 3, 5, 0, 5, 3, 1, 2], np.int32)
+    _run_steps(Workload(cfg, ranks=ranks), cfg.W + 5)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("kind,V", [("mamba2", 80), ("gdn", 128), ("kda", 128)])
 def test_single_sequence_all_dense_and_all_sketch(kind, V):
     cfg = _edge_cfg(kind, V, B=1)
     _run_steps(Workload(cfg, ranks=np.zeros(8, np.int32)), cfg.W + 3)
