@@ -182,6 +182,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="only the warmup and timed decode steps (for counter runs)")
+    ap.add_argument("--profile-dense", action="store_true",
+                    help="as --profile, with the full-state-read baseline's steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="copy 1 GiB device to device three times (scales the HBM byte counters)")
     ap.add_argument("--quiet", action="store_true")
@@ -286,6 +288,12 @@ def main():
     K = max(period, (args.steps + period - 1) // period * period)
     warm = max(0, args.warmup)
     # ---- whole decode steps (the headline) -----------------------------------
+    if args.profile_dense:
+        run_steps(warm, 0, dense=True)
+        ms = timed(lambda: run_steps(K, warm, dense=True))
+        print(json.dumps({"profile_run": "dense", "us_per_step": round(ms * 1000.0 / K, 3), "steps": K}),
+              flush=True)
+        return
     run_steps(warm, 0)
     torch.cuda.synchronize()
     ms = timed(lambda: run_steps(K, warm))
