@@ -161,7 +161,18 @@ def cpu_baseline(cfg, wl, steps=None, n_items: int = 16384):
             "kind": "oracle",
             "sample": f"{len(items)} of {cfg.B * cfg.H} (b,h) items ({per_head} random sequences per head), "
                       f"one window of {cfg.W} reads + 1 flush, fp64 numpy, 1 thread, {dt:.1f} s; scaled to all items",
-            "host_cpus_visible": len(os.sched_getaffinity(0))}
+            "host_cpus_visible": len(os.sched_getaffinity(0)), "cpu_model": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ---------------------------------------------------------------------------
