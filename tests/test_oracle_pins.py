@@ -392,7 +392,7 @@ def test_flushed_state_matches_wy_chunk_form(kind):
 # ---------------------------------------------------------------------------
 # the two oracle modes agree
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["c0", "c1", "c3", "c4"])
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3", "c4"])
 def test_item_and_batch_modes_agree(name):
     cfg = CONFIGS[name].with_batch(2)
     wl = Workload(cfg)
