@@ -45,6 +45,12 @@ Two evaluation modes, which the tests require to agree to 1e-12:
     Q = P F_r^T (so F_r q~ = Q^T q).  This is what the parity tests use at
     size.
 
+Parity unpinned: ``plan``'s frame order and bucket rule are this project's
+own (the pages define neither), so they are pinned only against a hand-worked
+example of that rule and against the library's independent planner, not
+against the pages; and the pages print no worked example of y, so absolute
+outputs are pinned through the exact special cases and closed forms instead.
+
 Readings where the pages are silent are listed in the project's design notes;
 the ones this file depends on: token j is read against the last flush with
 itself already applied (read, then flush after the W-th read); Z is formed from
@@ -81,6 +87,8 @@ def plan(rank: Sequence[int], group: Sequence[int], G: int, K: int,
     * bucket[h] = 0 for a dense head, else 1 + (r - 1) // 8;
     * order lists the heads: dense first, then buckets from high to low, head
       index ascending within a bucket.
+
+    Parity unpinned by the pages (the rule is ours; see the module header).
     """
     rank = [int(x) for x in rank]
     group = [int(x) for x in group]
