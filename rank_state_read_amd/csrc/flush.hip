@@ -28,7 +28,8 @@
 // operand -(T (gamma K)) and the 16 x V tile T V_w.  Once the state has landed
 // each wave only runs MFMAs on its own columns -- U (kept in registers, where
 // its accumulator layout is already the B operand of the update), the update,
-// the store, then Z -- with a single barrier, for the basis rows.
+// Z, then the store -- with no barrier unless the head's rank exceeds 16 (each
+// further 16-row basis tile is staged between two barriers).
 //
 // The state tiles serve directly as the B operand of the products with S: the
 // register index r of a tile is used as the 4-wide K step, which only permutes
@@ -403,13 +404,13 @@ void flush_kernel(FlushArgs A, HeadTable T) {
         }
     }
     // ---- 6. Z = Omega_r S for a sketch head, then the state store ----
-    // Z goes first: reading the basis rows makes the compiler wait for every
-    // outstanding memory operation, which at this point are only consumed
-    // state loads, not the stores.  Every wave waited for its own basis
-    // granules before its state load; the first window barrier (or the one
-    // below when there is no window) makes all of them visible.  The two
-    // cases keep separate tails so that no path reaches the stores with a
-    // state load the compiler still counts as outstanding.
+    // Z goes first: storing the state first needs no extra wait either, but
+    // measured slower (the block's stores then trail its Z work).  Every wave
+    // waited for its own first-tile basis granules before its state load; the
+    // first window barrier (or the one below when there is no window) makes
+    // all of them visible.  The two cases keep separate tails so that no path
+    // reaches the stores with a state load the compiler still counts as
+    // outstanding.
     auto sketch_rows = [&]() {
         float* Zi = A.Z + (size_t(T.zrow[p]) * A.B + size_t(b) * r) * V;
         const int mts = (r + 15) >> 4;
