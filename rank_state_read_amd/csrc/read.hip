@@ -92,11 +92,14 @@ __device__ __forceinline__ float raw_dot8(const typename Vec8<QT>::raw_t& a, con
     }
 }
 
-template <int KIND, int V, typename QT>
+template <int KIND, int V, typename QT, bool DEEP = false>
 struct RowSweep {
     static constexpr bool KDA = KIND == SKSSM_KDA;
     static constexpr bool DELTA = KIND != SKSSM_MAMBA2;
-    static constexpr int CH = KDA ? 1 : 2;  // window slots per round trip
+    // window slots per round trip: the bf16 GDN instances have registers to
+    // spare (a 96-VGPR budget), so with DEEP they fetch four slots at a time
+    static constexpr int CH =
+        KDA ? 1 : (DEEP && KIND == SKSSM_GDN && std::is_same<QT, Bf16Tag>::value) ? 4 : 2;
     static constexpr int NA = KDA ? 8 : 1;  // decay values per slot and lane
     using V8 = Vec8<QT>;
 
@@ -252,7 +255,7 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
     constexpr int VL = V / 8;
     constexpr bool M2 = KIND == SKSSM_MAMBA2;
     using V8 = Vec8<QT>;
-    using RS = RowSweep<KIND, V, QT>;
+    using RS = RowSweep<KIND, V, QT, !SEQ>;
     // LDS: kRows token staging rows, then the coefficient map
     constexpr int kMapOff4 = kRows * RS::kStageBytes / 16;
     char* stg = reinterpret_cast<char*>(lds4) + (threadIdx.x >> 4) * RS::kStageBytes;
@@ -322,7 +325,9 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
         for (int e = 0; e < 8; ++e) u[e] = gtot * q[e];
     }
 
-    // y = sum_m (F_m . q~) Z_m + intra, two sketch rows per round trip
+    // y = sum_m (F_m . q~) Z_m + intra, ZR sketch rows per round trip (four
+    // for the lockstep bf16 GDN instances, which have the registers, else two)
+    constexpr int ZR = (!SEQ && KIND == SKSSM_GDN && std::is_same<QT, Bf16Tag>::value) ? 4 : 2;
     for (int m0 = 0; m0 < r; m0 += kMapRows) {
         if (m0 > 0) {
             __syncthreads();  // every row is done with the previous piece
@@ -332,38 +337,30 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
         }
         const int mend = min(r, m0 + kMapRows);
         if (!active) continue;
-        for (int m = m0; m < mend; m += 2) {
-            float z0[8], z1[8];
+        for (int m = m0; m < mend; m += ZR) {
+            float z[ZR][8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                z0[e] = 0.f;
-                z1[e] = 0.f;
-            }
+            for (int j = 0; j < ZR; ++j)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) z[j][e] = 0.f;
             if (l < VL) {
-                load8f(Zi + size_t(m) * V + 8 * l, z0);
-                if (m + 1 < mend) load8f(Zi + size_t(m + 1) * V + 8 * l, z1);
+#pragma unroll
+                for (int j = 0; j < ZR; ++j)
+                    if (m + j < mend) load8f(Zi + size_t(m + j) * V + 8 * l, z[j]);
             }
-            {
-                float f[8];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    f[e] = fmap_s[(m - m0) * K + 4 * l + e];
-                    f[4 + e] = fmap_s[(m - m0) * K + K / 2 + 4 * l + e];
+            for (int j = 0; j < ZR; ++j) {
+                if (m + j < mend) {
+                    float f[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        f[e] = fmap_s[(m + j - m0) * K + 4 * l + e];
+                        f[4 + e] = fmap_s[(m + j - m0) * K + K / 2 + 4 * l + e];
+                    }
+                    const float cj = row_sum16(dot8(f, u));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) acc[e] = fmaf(cj, z[j][e], acc[e]);
                 }
-                const float c0 = row_sum16(dot8(f, u));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = fmaf(c0, z0[e], acc[e]);
-            }
-            if (m + 1 < mend) {
-                float f[8];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    f[e] = fmap_s[(m + 1 - m0) * K + 4 * l + e];
-                    f[4 + e] = fmap_s[(m + 1 - m0) * K + K / 2 + 4 * l + e];
-                }
-                const float c1 = row_sum16(dot8(f, u));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = fmaf(c1, z1[e], acc[e]);
             }
         }
     }
@@ -422,7 +419,7 @@ __device__ __forceinline__ void dense_block(const ReadArgs& A, const HeadTable& 
         if (owner && kk < K) sreg[j] = S4[kk * V4 + v4];
     }
     if (tid < 16) {
-        using RS = RowSweep<KIND, V, QT>;
+        using RS = RowSweep<KIND, V, QT, !SEQ>;
         char* stg = reinterpret_cast<char*>(lds4) + DenseLds<V>::bytes;
         typename V8::raw_t qr;
         float u[8], acc[8], g = 1.f;
