@@ -349,18 +349,43 @@ def main():
         seq_tabs.append((torch.from_numpy(pv).to(dev), torch.from_numpy(rows).to(dev),
                          torch.full((len(rows),), W, dtype=torch.int32, device=dev)))
 
-    def seq_steps(n, s0):
+    # with side=True each layer's row-list flush runs on a second stream (default
+    # priority), ordered after that layer's read and before its next read, so
+    # it can fill the CUs that the read's last blocks leave idle
+    side_stream = torch.cuda.Stream()
+    main_stream = torch.cuda.current_stream()
+    flush_done = [None] * NI
+
+    def seq_steps(n, s0, side=False):
         for s in range(s0, s0 + n):
-            L = lays[s % NI]
+            i = s % NI
+            L = lays[i]
             k = (s // NI) % W
             pv, rows, cnt = seq_tabs[k]
             d = inputs[k]
+            if flush_done[i] is not None:
+                main_stream.wait_event(flush_done[i])
+                flush_done[i] = None
             L.read_seq(pv, d["q"], d["k"], d["v"], d["a"], d["beta"])
             if rows.numel():
-                L.flush_seq(rows, cnt)
+                if side:
+                    ev = torch.cuda.Event()
+                    ev.record(main_stream)
+                    side_stream.wait_event(ev)
+                    L.flush_seq(rows, cnt, stream=side_stream)
+                    flush_done[i] = torch.cuda.Event()
+                    flush_done[i].record(side_stream)
+                else:
+                    L.flush_seq(rows, cnt)
+        for i in range(NI):
+            if flush_done[i] is not None:
+                main_stream.wait_event(flush_done[i])
+                flush_done[i] = None
 
     seq_steps(period, 0)
     seq_step_us = timed(lambda: seq_steps(K, 0)) * 1000.0 / K
+    seq_steps(period, 0, side=True)
+    seq_side_us = timed(lambda: seq_steps(K, 0, side=True)) * 1000.0 / K
 
     # ---- standard per-token decode: every token reads and writes the state ------
     def rmw(L, pos):
@@ -417,6 +442,7 @@ def main():
             "layer_ratio_dense_over_sketch": round(dense_step_us / us_step, 3),
             "model_token_us_all_layers": round(us_step * NI, 2) if args.layers else None,
             "continuous_batching_step_us": round(seq_step_us, 3),
+            "continuous_batching_step_us_flush_side_stream": round(seq_side_us, 3),
             "rmw_step_us": round(rmw_us, 2),
             "rmw_GBps": round(rmw_bytes(cfg) / (rmw_us * 1e3), 1),
             "ratio_rmw_over_sketch_step": round(rmw_us / us_step, 3),
