@@ -228,14 +228,14 @@ def test_dense_read_baseline(name, B):
 # ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------
-def _edge_cfg(kind, V, B=19, cap=49):
+def _edge_cfg(kind, V, B=19, cap=49, qkv="bf16"):
     return Config(f"edge-{kind}-{V}", kind, B=B, H=8, K=128, V=V, G=2, W=16, steps=40,
-                  qkv="bf16", mean_rank=6, rank_cap=cap, n_dense=0, seed=77)
+                  qkv=qkv, mean_rank=6, rank_cap=cap, n_dense=0, seed=77)
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("kind,V", [("mamba2", 80), ("mamba2", 64), ("gdn", 128), ("kda", 128),
-                                    ("kda", 80)])
+@pytest.mark.parametrize("kind,V", [("mamba2", 80), ("mamba2", 64), ("mamba2", 128), ("gdn", 128),
+                                    ("gdn", 80), ("gdn", 64), ("kda", 128), ("kda", 80), ("kda", 64)])
 def test_rank_extremes(kind, V):
     """Ranks at 1, at tile edges (16, 17, 32, 33), at the cap, mixed with dense heads."""
     cfg = _edge_cfg(kind, V, cap=64)
@@ -409,3 +409,12 @@ def test_max_heads():
     cfg = Config("edge-h256", "mamba2", B=3, H=256, K=128, V=64, G=16, W=16, steps=20, qkv="bf16",
                  mean_rank=6, rank_cap=49, n_dense=5, seed=78)
     _run_steps(Workload(cfg), cfg.W + 4)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("kind,V", [("mamba2", 128), ("gdn", 128), ("gdn", 80), ("kda", 128), ("kda", 64)])
+def test_fp32_qkv(kind, V):
+    """The float32 q/k/v instances of every family (the headline layers use bf16)."""
+    cfg = _edge_cfg(kind, V, qkv="f32")
+    ranks = np.array([1, 16, 0, 17, 49, 6, 3, 0], np.int32)
+    _run_steps(Workload(cfg, ranks=ranks), cfg.W + 5)
