@@ -86,3 +86,13 @@ def test_rmw_full_size_sampled(name):
     items = sorted({(0, 0), (c.B - 1, c.H - 1)} |
                    {(int(rng.integers(c.B)), int(rng.integers(c.H))) for _ in range(30)})
     _run(wl, 6, items=items)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("kind,V,qkv", [("mamba2", 64, "bf16"), ("gdn", 64, "bf16"), ("kda", 80, "bf16"),
+                                        ("mamba2", 128, "f32"), ("gdn", 80, "f32"), ("kda", 128, "f32")])
+def test_rmw_widths_and_dtypes(kind, V, qkv):
+    from workloads import Config
+    cfg = Config(f"rmw-{kind}-{V}-{qkv}", kind, B=19, H=8, K=128, V=V, G=2, W=16, steps=20, qkv=qkv,
+                 mean_rank=6, rank_cap=49, n_dense=0, seed=79)
+    _run(Workload(cfg), 20)
