@@ -30,7 +30,7 @@ if ROOT not in sys.path:
 
 METRIC = "per-layer decode µs + achieved HBM GB/s, Nano-9B layer, batch 256, mean rank 6"
 HBM_PEAK_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "read_kernel_c1_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "read_kernel_{}_traffic.md")  # per workload
 READ_SOURCES = [os.path.join(ROOT, "rank_state_read_amd", "csrc", f)
                 for f in ("read.hip", "device_common.h", "sketchssm_internal.h")]
 
@@ -49,7 +49,7 @@ def measured_traffic(config: str):
     taken on this workload and on the read kernel as it is now (same source
     hash), else None."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(TRAFFIC_FILE.format(config)).read()
     except OSError:
         return None
     keys = ("workload:", "source_hash:", "hbm_bytes_per_launch:")
