@@ -395,6 +395,14 @@ def main():
     [rmw(L, 0) for L in lays]
     rmw_us = timed(lambda: [rmw(L, p) for p in range(W) for L in lays], reps=2) * 1000.0 / (NI * W)
 
+    # ---- a device-to-device copy of 1 GiB: the practical read+write HBM rate on this GPU
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    copy_us = timed(lambda: dst.copy_(src), reps=5) * 1000.0
+    copy_GBps = 2 * src.numel() * 4 / (copy_us * 1e3)
+    del src, dst
+
     ranks = wl.ranks
     rb = [read_bytes(cfg, ranks, p) for p in range(W)]
     read_GBps = float(np.mean([b / (t * 1e3) for b, t in zip(rb, per_pos)]))
@@ -422,7 +430,8 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "read_kernel (sketchssm_decode_read)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(cfg.name),
-                     "bytes_per_launch": int(rb_avg), "avg_launch_us": round(read_us, 3)},
+                     "bytes_per_launch": int(rb_avg), "avg_launch_us": round(read_us, 3),
+                     "measured_copy_GBps": round(copy_GBps, 1), "frac_of_measured_copy": round(achieved / copy_GBps, 4)},
         "detail": {
             "read_us_mean": round(read_us, 3),
             "read_us_per_pos": [round(x, 2) for x in per_pos],
