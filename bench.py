@@ -200,8 +200,8 @@ def main():
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the decode path has no cross-GPU exchange and this "
-              "build runs on a single MI355X (use --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU only: the decode path has no cross-GPU exchange and the "
+              "benchmark runs on a single MI355X (use --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import torch
