@@ -185,8 +185,9 @@ void flush_kernel(FlushArgs A, HeadTable T) {
     // from r up to the next multiple of 16 repeat row r - 1: they only feed
     // sketch rows that are never stored.  Holding one tile instead of the
     // largest rank's rows keeps the block's LDS small enough that registers,
-    // not LDS, bound the resident blocks (c1: four 320-thread blocks per CU
-    // instead of three).  The first tile is requested here, with the window.
+    // not LDS, bound the resident blocks (a V = 80 Mamba-2 layer whose largest
+    // rank is 49: four 320-thread blocks per CU instead of three).  The first
+    // tile is requested here, with the window.
     auto stage_basis = [&](int mt) {
         const float* om = A.basis + size_t(g) * A.basis_rows * K;
 #pragma unroll
