@@ -270,12 +270,20 @@ def main():
     def dense_flush(L, n):
         Bnd.sketchssm_flush(dense_plan, L.S, None, None, L.kbuf, L.vbuf, L.abuf, L.bbuf, n)
 
-    def run_steps(n, s0, dense=False):
-        """n layer steps starting at global step s0 (instance s % NI, position (s // NI) % W)."""
+    def read_flush(L, dense=False):
+        d = inputs[W - 1]
+        return L.read_flush(d["q"], d["k"], d["v"], d["a"], d["beta"], plan=dense_plan if dense else None)
+
+    def run_steps(n, s0, dense=False, fused=True):
+        """n layer steps starting at global step s0 (instance s % NI, position (s // NI) % W).
+        fused: the window's last read and its flush in one call (the library fuses
+        them where that pays), else the read and then the flush."""
         for s in range(s0, s0 + n):
             L = lays[s % NI]
             pos = (s // NI) % W
-            if dense:
+            if fused and pos == W - 1:
+                read_flush(L, dense)
+            elif dense:
                 dense_read(L, pos)
                 if pos == W - 1:
                     dense_flush(L, W)
@@ -299,10 +307,18 @@ def main():
     K = max(period, (args.steps + period - 1) // period * period)
     warm = max(0, args.warmup)
     # ---- whole decode steps (the headline) -----------------------------------
+    # counter runs launch the read at every window position and the plain flush
+    # (the fused last read is profiled by the kernel trace of a default run)
     if args.profile_dense:
-        run_steps(warm, 0, dense=True)
-        ms = timed(lambda: run_steps(K, warm, dense=True))
+        run_steps(warm, 0, dense=True, fused=False)
+        ms = timed(lambda: run_steps(K, warm, dense=True, fused=False))
         print(json.dumps({"profile_run": "dense", "us_per_step": round(ms * 1000.0 / K, 3), "steps": K}),
+              flush=True)
+        return
+    if args.profile:
+        run_steps(warm, 0, fused=False)
+        ms = timed(lambda: run_steps(K, warm, fused=False))
+        print(json.dumps({"profile_run": True, "us_per_step": round(ms * 1000.0 / K, 3), "steps": K}),
               flush=True)
         return
     run_steps(warm, 0)
@@ -310,9 +326,6 @@ def main():
     ms = timed(lambda: run_steps(K, warm))
     us_step = ms * 1000.0 / K
     log(f"sketch path: {us_step:.2f} us/step over {K} steps")
-    if args.profile:
-        print(json.dumps({"profile_run": True, "us_per_step": round(us_step, 3), "steps": K}), flush=True)
-        return
 
     # ---- the read kernel alone, per window position ---------------------------
     per_pos = []
@@ -326,11 +339,17 @@ def main():
     # ---- the flush alone (re-applies the same window; the time is what matters) --
     flush_us = timed(lambda: [L.flush(W) for L in lays], reps=4) * 1000.0 / NI
     init_us = timed(lambda: [L.flush(0) for L in lays], reps=4) * 1000.0 / NI
+    read_flush_us = timed(lambda: [read_flush(L) for L in lays], reps=4) * 1000.0 / NI
+    # the same steps with the last read and the flush as two calls
+    run_steps(period, 0, fused=False)
+    unfused_step_us = timed(lambda: run_steps(K, 0, fused=False)) * 1000.0 / K
 
     # ---- full-state-read baseline (every head dense) ----------------------------
     run_steps(period, 0, dense=True)
     ms_d = timed(lambda: run_steps(K, 0, dense=True))
     dense_step_us = ms_d * 1000.0 / K
+    run_steps(period, 0, dense=True, fused=False)
+    dense_unfused_step_us = timed(lambda: run_steps(K, 0, dense=True, fused=False)) * 1000.0 / K
     dense_pos = []
     for pos in (0, W // 2, W - 1):
         dense_pos.append(timed(lambda pos=pos: [dense_read(L, pos) for L in lays], reps=4) * 1000.0 / NI)
@@ -439,7 +458,10 @@ def main():
             "flush_us": round(flush_us, 2),
             "flush_GBps": round(fb / (flush_us * 1e3), 1),
             "initial_sketch_us": round(init_us, 2),
-            "layer_us_model": round(read_us + flush_us / W, 3),
+            "read_flush_us": round(read_flush_us, 2),
+            "layer_us_model": round((sum(per_pos[:-1]) + read_flush_us) / W, 3),
+            "step_us_last_read_and_flush_apart": round(unfused_step_us, 3),
+            "dense_step_us_last_read_and_flush_apart": round(dense_unfused_step_us, 3),
             "step_bytes": int(sb),
             "dense_step_us": round(dense_step_us, 3),
             "dense_read_us_mean": round(dense_read_us, 3),

@@ -218,6 +218,33 @@ sketchssm_status sketchssm_flush_seq(const sketchssm_plan* plan, float* S, float
                                      const int32_t* n_tokens, int32_t n_seqs, void* stream);
 
 /*
+ * The window's last read and its flush in one pass: equivalent to
+ * sketchssm_decode_read at pos = W-1 followed by sketchssm_flush(n_tokens = W)
+ * on the same stream, with the same outputs.  The flush already holds the
+ * state at the last flush, the updated state and the window, so the token's
+ * carried-back query q~ = (M_W ... M_1)^T q comes from the chunked form of the
+ * update, and the sketch read is Z_old^T (F q~) + (S_n^T q - S_0^T q~), the
+ * bracket being the buffered tokens' exact term (Abstract of "SketchSSM: Write
+ * to the Full State, Read from a Compact Sketch": buffered keys and values,
+ * reads from the stored sketch; dense heads output S_n^T q).  The window's
+ * slots 0 .. W-2 are read; the current token is taken from q, k, v, a, beta
+ * (the window restarts at slot 0 afterwards).  One pass for Mamba-2 and KDA;
+ * for GDN, where the fused pass measured slower, the same call runs the read
+ * and then the flush.
+ *   S, Z          as in sketchssm_flush (Z is read as the old sketch, then
+ *                 overwritten with the new one)
+ *   frames        as in sketchssm_decode_read; basis as in sketchssm_flush
+ *   q, k, v, a, beta, y   as in sketchssm_decode_read
+ *   kbuf .. bbuf  the window: slots 0 .. W-2 are read; slot W-1 may be written
+ */
+sketchssm_status sketchssm_decode_read_flush(const sketchssm_plan* plan, float* S, float* Z,
+                                             const float* frames, const float* basis,
+                                             const void* q, const void* k, const void* v,
+                                             const float* a, const float* beta, void* kbuf,
+                                             void* vbuf, float* abuf, float* bbuf, float* y,
+                                             void* stream);
+
+/*
  * Full-state-read baseline: sketchssm_decode_read with every head dense (each
  * query reads S_0; the ReplaySSM-style read that the Abstract contrasts with).
  * Arguments as in sketchssm_decode_read; the shape replaces the plan.

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     lib,
     make_shape,
     sketchssm_decode_read,
+    sketchssm_decode_read_flush,
     sketchssm_decode_read_seq,
     sketchssm_dense_read,
     sketchssm_flush,

@@ -52,6 +52,7 @@ _PROTOS = {
     "sketchssm_rmw_step": (c_i32, [ctypes.POINTER(Shape)] + [c_vp] * 8),
     "sketchssm_decode_read_seq": (c_i32, [c_vp] * 16),
     "sketchssm_flush_seq": (c_i32, [c_vp] * 10 + [c_i32, c_vp]),
+    "sketchssm_decode_read_flush": (c_i32, [c_vp] * 16),
     "sketchssm_status_string": (ctypes.c_char_p, [c_i32]),
 }
 
@@ -200,3 +201,11 @@ def sketchssm_flush_seq(plan: Plan, S, Z, basis, kbuf, vbuf, abuf, bbuf, seqs, n
            lib().sketchssm_flush_seq(plan.handle, _ptr(S), _ptr(Z), _ptr(basis), _ptr(kbuf), _ptr(vbuf),
                                      _ptr(abuf), _ptr(bbuf), _ptr(seqs), _ptr(n_tokens), int(n_seqs),
                                      _stream(stream)))
+
+
+def sketchssm_decode_read_flush(plan: Plan, S, Z, frames, basis, q, k, v, a, beta, kbuf, vbuf, abuf, bbuf, y,
+                                stream=None):
+    _check("sketchssm_decode_read_flush",
+           lib().sketchssm_decode_read_flush(plan.handle, _ptr(S), _ptr(Z), _ptr(frames), _ptr(basis), _ptr(q),
+                                             _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(kbuf), _ptr(vbuf),
+                                             _ptr(abuf), _ptr(bbuf), _ptr(y), _stream(stream)))

@@ -58,11 +58,20 @@ struct FlushArgs {
     int Hk, share;  // key heads; each serves `share` consecutive heads
     int nb;   // blocks per head: B, or the number of listed rows
     int omt;  // basis tiles held in LDS: 1 when the plan has sketch heads, else 0
+    // the fused last read: the token at window position W-1 (not appended; it is
+    // the window's last slot), the coefficient maps and the output
+    const void* tq;
+    const void* tk;
+    const void* tv;
+    const float* ta;
+    const float* tb;
+    const float* frames;
+    float* y;
 };
 
 // LDS map, in floats.  Row strides are 4 (mod 16) floats: the rows 4 (l/16) + s
 // that the four quarter-waves read then start 16 banks apart.
-template <int KIND, int V>
+template <int KIND, int V, bool FUSED = false>
 struct FlushLds {
     static constexpr bool delta = KIND != SKSSM_MAMBA2;
     static constexpr bool kda = KIND == SKSSM_KDA;
@@ -77,8 +86,25 @@ struct FlushLds {
     static constexpr int tm = lt + (delta ? 256 : 0);      // delta: T [16][16]
     static constexpr int al = tm + (delta ? 256 : 0);      // KDA: decays [16][K]
     static constexpr int om = al + (kda ? 16 * kK : 0);    // one tile of basis rows [16][K], swizzled
-    static size_t bytes(int omt) { return size_t(om + 16 * omt * kK) * 4; }
+    // fused last read: the query, q~ (delta), (sigma K) q, T^T (sigma K) q, c = F q~,
+    // and one 16-row tile of the coefficient map
+    static constexpr int qs = om + 16 * kK;
+    static constexpr int qt = qs + (FUSED ? kK : 0);
+    static constexpr int ws = qt + (FUSED && delta ? kK : 0);
+    static constexpr int ts = ws + (FUSED ? 16 : 0);
+    static constexpr int cs = ts + (FUSED ? 16 : 0);
+    static constexpr int fm = cs + (FUSED ? 16 : 0);
+    static size_t bytes(int omt) {
+        return FUSED ? size_t(fm + 16 * kK) * 4 : size_t(om + 16 * omt * kK) * 4;
+    }
 };
+
+// Sum over the four lanes l % 16 + 16 j; every lane gets the same bits.
+__device__ __forceinline__ float quarter_sum4(float x) {
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
 
 __device__ __forceinline__ float read_lane(float x, int l) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
@@ -98,11 +124,15 @@ __device__ __forceinline__ float pick(const float (&x)[N], int i) {
 // V = 128 kernels per CU, four of the 320-thread V = 80 ones.
 constexpr int kFlushWavesPerEu = 6;
 
-template <int KIND, int V, typename QT>
-__global__ __launch_bounds__(V / 16 * 64) __attribute__((amdgpu_waves_per_eu(kFlushWavesPerEu)))
+// FUSED: the read of the window's last token and the flush of the full window
+// in one pass (see sketchssm_decode_read_flush; Mamba-2 and KDA); the KDA
+// instances then take a 96-VGPR budget.
+template <int KIND, int V, typename QT, bool FUSED>
+__global__ __launch_bounds__(V / 16 * 64)
+__attribute__((amdgpu_waves_per_eu((FUSED && KIND != SKSSM_MAMBA2) ? 5 : kFlushWavesPerEu)))
 void flush_kernel(FlushArgs A, HeadTable T) {
     using V8 = Vec8<QT>;
-    using L = FlushLds<KIND, V>;
+    using L = FlushLds<KIND, V, FUSED>;
     constexpr int K = kK;
     constexpr int W = kW;
     constexpr int NW = V / 16;
@@ -122,6 +152,12 @@ void flush_kernel(FlushArgs A, HeadTable T) {
     float* Tm = sm + L::tm;
     float* Al = sm + L::al;
     float* Om = sm + L::om;
+    float* Qs = sm + L::qs;  // fused: the query
+    float* Qt = sm + L::qt;  // fused, delta rule: q~
+    float* Ws = sm + L::ws;  // fused, delta rule: (sigma K) q
+    float* Ts = sm + L::ts;  // fused, delta rule: T^T (sigma K) q
+    float* Cs = sm + L::cs;  // fused: c = F q~ of the current map tile
+    float* Fm = sm + L::fm;  // fused: one 16-row tile of the coefficient map
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -148,6 +184,25 @@ void flush_kernel(FlushArgs A, HeadTable T) {
     auto wslot = [&](int i) { return (size_t(i) * A.H + h) * A.B + b; };
     auto wslotk = [&](int i) { return (size_t(i) * A.Hk + h / A.share) * A.B + b; };
 
+    // fused: coefficient-map rows 16 mt .. 16 mt + 15 into Fm (natural order;
+    // rows from r up repeat row r - 1 and are never used)
+    auto stage_fmap = [&](int mt) {
+        const float* fsrc = A.frames + size_t(T.frow[p]) * K;
+        const int wq = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+        for (int jf = 0; jf < (8 + NW - 1) / NW; ++jf) {
+            const int qd = wq + jf * NW;  // 64-granule chunk: tile rows 2 qd, 2 qd + 1
+            if (qd < 8) {
+                const int gi = 64 * qd + lane;
+                const int row = 16 * mt + (gi >> 5);
+                const int srow = row < r ? row : r - 1;
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void*)(fsrc + size_t(srow) * K + 4 * (gi & 31)),
+                    (__attribute__((address_space(3))) void*)(Fm + 256 * qd), 16, 0, 0);
+            }
+        }
+    };
+
     // ---- 1. window loads into registers, issued first ----
     // Every slot is fetched (the window always holds W slots) and slots >= n
     // are masked where the values are used: the loads then need no branches,
@@ -165,17 +220,46 @@ void flush_kernel(FlushArgs A, HeadTable T) {
     float4 a4[NA];
     const int ki = tid >> 4, kc0 = (tid & 15) * 8;            // key chunk of this thread
     const int vi = tid / (V / 8), vc0 = (tid % (V / 8)) * 8;  // value chunk of this thread
+    const size_t itemk = size_t(b) * A.Hk + h / A.share;  // (b, key head)
     if (n > 0) {
-        if (!KDA) as_l = A.abuf[wslot(lane & 15)];
-        if (DELTA) bs_l = A.bbuf[wslot(lane & 15)];
-        if (tid < KCH) kraw = V8::load(A.kbuf, wslotk(ki) * K + kc0);
-        if (tid < VCH) vraw = V8::load(A.vbuf, wslot(vi) * V + vc0);
+        // fused: slot W-1 is the current token, read from its inputs (the
+        // source address is selected, so the loads stay outside branches)
+        const bool cur_s = FUSED && (lane & 15) == W - 1;
+        if (!KDA) as_l = cur_s ? A.ta[item] : A.abuf[wslot(lane & 15)];
+        if (DELTA) bs_l = cur_s ? A.tb[item] : A.bbuf[wslot(lane & 15)];
+        if (tid < KCH) {
+            const bool cur = FUSED && ki == W - 1;
+            kraw = V8::load(cur ? A.tk : A.kbuf, cur ? itemk * K + kc0 : wslotk(ki) * K + kc0);
+        }
+        if (tid < VCH) {
+            const bool cur = FUSED && vi == W - 1;
+            vraw = V8::load(cur ? A.tv : A.vbuf, cur ? item * V + vc0 : wslot(vi) * V + vc0);
+        }
         if (KDA) {
 #pragma unroll
             for (int j = 0; j < NA; ++j) {
                 const int c = tid + j * NT;
-                if (c < ACH) a4[j] = *reinterpret_cast<const float4*>(A.abuf + wslot(c >> 5) * K + (c & 31) * 4);
+                const bool cur = FUSED && (c >> 5) == W - 1;
+                const float* src = cur ? A.ta + item * K : A.abuf + wslot(c >> 5) * K;
+                if (c < ACH) a4[j] = *reinterpret_cast<const float4*>(src + (c & 31) * 4);
             }
+        }
+    }
+    // fused: the query (16 threads, 8 elements each), the first 16 sketch rows
+    // of the old sketch for this lane's column (rows lq + 4 j) and the first
+    // 16 rows of the coefficient map (straight into LDS)
+    typename V8::raw_t qraw = V8::zero();
+    float zo[4] = {0.f, 0.f, 0.f, 0.f};
+    const float* Zold = sketch ? A.Z + (size_t(T.zrow[p]) * A.B + size_t(b) * r) * V : nullptr;
+    if (FUSED) {
+        if (tid < K / 8) qraw = V8::load(A.tq, itemk * K + 8 * tid);
+        if (sketch) {
+#pragma unroll
+            for (int jz = 0; jz < 4; ++jz) {
+                const int m = min(lq + 4 * jz, r - 1);  // rows >= r are loaded but not used
+                zo[jz] = Zold[size_t(m) * V + v0 + lr];
+            }
+            stage_fmap(0);
         }
     }
 
@@ -236,7 +320,14 @@ void flush_kernel(FlushArgs A, HeadTable T) {
     }
     float gamW = 1.f;
     f32x4 u = {0.f, 0.f, 0.f, 0.f};
+    float zc = 0.f;     // fused: sum_m c_m Z_old[m][column], this lane's column
+    float intra = 0.f;  // fused: the buffered tokens' term of the last read, same column
     if (n > 0) {
+        if (FUSED && tid < K / 8) {
+            float f[8];
+            V8::unpack(qraw, f);
+            store8f(Qs + 8 * tid, f);
+        }
         if (tid < VCH) {
             float f[8];
             V8::unpack(vraw, f);
@@ -373,6 +464,70 @@ void flush_kernel(FlushArgs A, HeadTable T) {
             }
             __syncthreads();
         }
+        if (FUSED) {
+            // With the state after the window S_n = P S_0 + X, P = M_W ... M_1 =
+            // diag(gamma_W) - (sigma K)^T T (gamma K) and X = (sigma K)^T (T V_w)
+            // (Mamba-2: P = gamma_W I, X = (sigma K)^T V_w), the last token's
+            // buffered-token term is X^T q = (T V_w)^T w with w = (sigma K) q,
+            // and its carried-back query is q~ = P^T q = gamma_W q - (gamma K)^T T^T w.
+            {
+                const int i = tid >> 4, l16 = tid & 15;
+                if (i < W) {
+                    float k8[8], q8[8];
+                    load8f(Kt + i * KS + 8 * l16, k8);
+                    load8f(Qs + 8 * l16, q8);
+                    const float wi = row_sum16(dot8(k8, q8));
+                    if (l16 == 0) Ws[i] = wi;
+                }
+            }
+            __syncthreads();
+            // this lane's column of X^T q: its four token rows 4 lq + rr
+            {
+                float ip = 0.f;
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr)
+                    ip = fmaf(Ws[4 * lq + rr], DELTA ? u[rr] : Vw[(4 * lq + rr) * VS + v0 + lr], ip);
+                intra = quarter_sum4(ip);
+            }
+            if (DELTA && sketch) {
+                if (tid < W) {
+                    float t = 0.f;
+#pragma unroll
+                    for (int i = 0; i < W; ++i) t = fmaf(Tm[i * 16 + tid], Ws[i], t);
+                    Ts[tid] = t;
+                }
+                __syncthreads();
+                if (tid < K) {
+                    float x = (KDA ? Gw[tid] : gamW) * Qs[tid];
+#pragma unroll
+                    for (int i = 0; i < W; ++i) x = fmaf(-Ts[i], Kg[i * KS + tid], x);
+                    Qt[tid] = x;
+                }
+                __syncthreads();
+            }
+            if (sketch) {
+                // c = F q~ for map rows 0 .. 15 (the tile landed with the window
+                // and the window barriers made it visible), then this lane's
+                // part of sum_m c_m Z_old[m][column]
+                {
+                    const int m = tid >> 4, l16 = tid & 15;
+                    if (m < 16) {
+                        float f8[8], q8[8];
+                        load8f(Fm + m * K + 8 * l16, f8);
+                        load8f((DELTA ? Qt : Qs) + 8 * l16, q8);
+                        float cm = row_sum16(dot8(f8, q8));
+                        if (!DELTA) cm *= gamW;
+                        if (l16 == 0) Cs[m] = cm;
+                    }
+                }
+                __syncthreads();
+                float zp = 0.f;
+#pragma unroll
+                for (int jz = 0; jz < 4; ++jz)
+                    if (lq + 4 * jz < r) zp = fmaf(Cs[lq + 4 * jz], zo[jz], zp);
+                zc = quarter_sum4(zp);
+            }
+        }
     }
     // nothing that reads the state may be scheduled above this point
     __builtin_amdgcn_sched_barrier(0);
@@ -403,6 +558,52 @@ void flush_kernel(FlushArgs A, HeadTable T) {
             }
             s[kt] = acc;
         }
+    }
+    // fused: the last token's output.  A dense head reads S_n^T q exactly; a
+    // sketch head outputs Z_old^T (F q~) + X^T q (both formed above while the
+    // state was in flight, plus the map tiles beyond the first).
+    if (FUSED) {
+        float yv;
+        if (sketch) {
+            for (int mt = 1; 16 * mt < r; ++mt) {  // ranks above 16
+                __syncthreads();  // every row is done with the previous tile
+                stage_fmap(mt);
+                float zm[4];
+#pragma unroll
+                for (int jz = 0; jz < 4; ++jz)
+                    zm[jz] = Zold[size_t(min(16 * mt + lq + 4 * jz, r - 1)) * V + v0 + lr];
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the tile and the rows
+                __syncthreads();
+                {
+                    const int m = tid >> 4, l16 = tid & 15;
+                    if (m < 16) {
+                        float f8[8], q8[8];
+                        load8f(Fm + m * K + 8 * l16, f8);
+                        load8f((DELTA ? Qt : Qs) + 8 * l16, q8);
+                        float cm = row_sum16(dot8(f8, q8));
+                        if (!DELTA) cm *= gamW;
+                        if (l16 == 0) Cs[m] = cm;
+                    }
+                }
+                __syncthreads();
+                float zp = 0.f;
+#pragma unroll
+                for (int jz = 0; jz < 4; ++jz)
+                    if (16 * mt + lq + 4 * jz < r) zp = fmaf(Cs[lq + 4 * jz], zm[jz], zp);
+                zc += quarter_sum4(zp);
+            }
+            yv = zc + intra;
+        } else {
+            float yp = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt) {
+                const f32x4 q4 = *reinterpret_cast<const f32x4*>(Qs + 16 * kt + 4 * lq);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) yp = fmaf(s[kt][rr], q4[rr], yp);
+            }
+            yv = quarter_sum4(yp);
+        }
+        if (lq == 0) A.y[item * V + v0 + lr] = yv;
     }
     // ---- 6. Z = Omega_r S for a sketch head, then the state store ----
     // Z goes first: storing the state first needs no extra wait either, but
@@ -454,11 +655,11 @@ void flush_kernel(FlushArgs A, HeadTable T) {
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-template <int KIND, int V, typename QT>
-static hipError_t launch_flush_t(const FlushArgs& a, const HeadTable& t, int grid,
+template <int KIND, int V, typename QT, bool FUSED>
+static hipError_t launch_flush_f(const FlushArgs& a, const HeadTable& t, int grid,
                                  hipStream_t s) {
-    const size_t lds = FlushLds<KIND, V>::bytes(a.omt);
-    auto fn = flush_kernel<KIND, V, QT>;
+    const size_t lds = FlushLds<KIND, V, FUSED>::bytes(a.omt);
+    auto fn = flush_kernel<KIND, V, QT, FUSED>;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                                  hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -467,6 +668,17 @@ static hipError_t launch_flush_t(const FlushArgs& a, const HeadTable& t, int gri
     }
     hipLaunchKernelGGL(fn, dim3(grid), dim3(V / 16 * 64), lds, s, a, t);
     return hipGetLastError();
+}
+
+template <int KIND, int V, typename QT>
+static hipError_t launch_flush_t(const FlushArgs& a, const HeadTable& t, int grid,
+                                 hipStream_t s) {
+    if (!a.y) return launch_flush_f<KIND, V, QT, false>(a, t, grid, s);
+    if constexpr (KIND == SKSSM_GDN) {
+        return hipErrorInvalidValue;  // GDN runs the last read and the flush apart
+    } else {
+        return launch_flush_f<KIND, V, QT, true>(a, t, grid, s);
+    }
 }
 
 template <int KIND, typename QT>
@@ -495,11 +707,22 @@ static hipError_t launch_flush_k(int kind, int V, const FlushArgs& a, const Head
 
 using namespace skssm;
 
+// The fused last read's extra arguments (null for a plain flush).
+struct FusedRead {
+    const float* frames;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* a;
+    const float* beta;
+    float* y;
+};
+
 static sketchssm_status run_flush(const sketchssm_plan* plan, float* S, float* Z,
                                   const float* basis, const void* kbuf, const void* vbuf,
                                   const float* abuf, const float* bbuf, int32_t n_tokens,
                                   const int32_t* seqs, const int32_t* ntok, int32_t n_seqs,
-                                  void* stream) {
+                                  void* stream, const FusedRead* fr = nullptr) {
     if (!plan) return SKSSM_EINVAL;
     const sketchssm_shape& sh = plan->shape;
     const bool delta = sh.kind != SKSSM_MAMBA2;
@@ -519,6 +742,14 @@ static sketchssm_status run_flush(const sketchssm_plan* plan, float* S, float* Z
         if (ptr && !aligned16(ptr)) return SKSSM_EALIGN;
     if (listed && ((reinterpret_cast<uintptr_t>(seqs) | reinterpret_cast<uintptr_t>(ntok)) & 3u))
         return SKSSM_EALIGN;
+    if (fr) {
+        if (!fr->q || !fr->k || !fr->v || !fr->a || !fr->y) return SKSSM_EINVAL;
+        if (delta != (fr->beta != nullptr)) return SKSSM_EINVAL;
+        if (n_sketch > 0 && !fr->frames) return SKSSM_EINVAL;
+        const void* fptrs[] = {fr->frames, fr->q, fr->k, fr->v, fr->a, fr->beta, fr->y};
+        for (const void* ptr : fptrs)
+            if (ptr && !aligned16(ptr)) return SKSSM_EALIGN;
+    }
     if (listed && n_seqs == 0) return SKSSM_OK;
     if (!listed && n_sketch == 0 && n_tokens == 0) return SKSSM_OK;  // nothing to write
 
@@ -540,6 +771,13 @@ static sketchssm_status run_flush(const sketchssm_plan* plan, float* S, float* Z
     A.Hk = kq_heads_of(sh);
     A.share = sh.H / A.Hk;
     A.omt = n_sketch > 0 ? 1 : 0;
+    A.tq = fr ? fr->q : nullptr;
+    A.tk = fr ? fr->k : nullptr;
+    A.tv = fr ? fr->v : nullptr;
+    A.ta = fr ? fr->a : nullptr;
+    A.tb = fr ? fr->beta : nullptr;
+    A.frames = fr ? fr->frames : nullptr;
+    A.y = fr ? fr->y : nullptr;
     const long grid = long(A.nb) * sh.H;
     if (grid > 0x7fffffffL) return SKSSM_ESHAPE;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -565,4 +803,26 @@ extern "C" sketchssm_status sketchssm_flush_seq(const sketchssm_plan* plan, floa
                                                 void* stream) {
     if (!seqs) return SKSSM_EINVAL;
     return run_flush(plan, S, Z, basis, kbuf, vbuf, abuf, bbuf, 0, seqs, n_tokens, n_seqs, stream);
+}
+
+extern "C" sketchssm_status sketchssm_decode_read_flush(const sketchssm_plan* plan, float* S, float* Z,
+                                                       const float* frames, const float* basis,
+                                                       const void* q, const void* k, const void* v,
+                                                       const float* a, const float* beta, void* kbuf,
+                                                       void* vbuf, float* abuf, float* bbuf, float* y,
+                                                       void* stream) {
+    if (!plan) return SKSSM_EINVAL;
+    if (plan->shape.kind == SKSSM_GDN) {
+        // For GDN the fused pass needs a 96-VGPR budget, which costs the flush a
+        // third of its resident blocks and more than the separate last read
+        // (measured 302 against 256 + 23 us at 256 x 32 heads): read, then flush.
+        const sketchssm_status st = sketchssm_decode_read(plan, S, Z, frames, q, k, v, a, beta, kbuf,
+                                                          vbuf, abuf, bbuf, plan->shape.W - 1, y,
+                                                          stream);
+        if (st != SKSSM_OK) return st;
+        return sketchssm_flush(plan, S, Z, basis, kbuf, vbuf, abuf, bbuf, plan->shape.W, stream);
+    }
+    const FusedRead fr{frames, q, k, v, a, beta, y};
+    return run_flush(plan, S, Z, basis, kbuf, vbuf, abuf, bbuf, plan->shape.W, nullptr, nullptr, 0,
+                     stream, &fr);
 }

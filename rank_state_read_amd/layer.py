@@ -97,6 +97,17 @@ class SketchLayer:
                                 self.vbuf, self.abuf, self.bbuf, pos, y, stream)
         return y
 
+    def read_flush(self, q, k, v, a, beta=None, y=None, stream=None, plan=None) -> torch.Tensor:
+        """The window's last read and its flush in one pass (``plan``: e.g. an
+        all-dense plan for the full-state-read baseline)."""
+        y = self.y if y is None else y
+        pl = self.plan if plan is None else plan
+        _b.sketchssm_decode_read_flush(pl, self.S, self.Z if plan is None else None,
+                                      self.frames if plan is None else None,
+                                      self.basis if plan is None else None, q, k, v, a, beta, self.kbuf,
+                                      self.vbuf, self.abuf, self.bbuf, y, stream)
+        return y
+
     def dense_read(self, pos: int, q, k, v, a, beta=None, y=None, stream=None) -> torch.Tensor:
         y = self.y if y is None else y
         _b.sketchssm_dense_read(self.shape, self.S, q, k, v, a, beta, self.kbuf, self.vbuf, self.abuf,

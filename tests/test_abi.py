@@ -185,6 +185,28 @@ def test_seq_entry_points_argument_errors():
     assert L.sketchssm_flush_seq(h, *fl, FAKE + 2, FAKE, 1, None) == 3
 
 
+def test_read_flush_argument_errors():
+    L = B.lib()
+    plan = B.Plan(_shape(), np.array([0, 1, 2, 3, 4, 5, 6, 7]), np.zeros(8, np.int32))
+    h = plan.handle
+    # S Z frames basis q k v a beta kbuf vbuf abuf bbuf y
+    ok = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE]
+
+    def call(**over):
+        names = ["S", "Z", "frames", "basis", "q", "k", "v", "a", "beta", "kbuf", "vbuf", "abuf", "bbuf", "y"]
+        a = dict(zip(names, ok))
+        a.update(over)
+        return L.sketchssm_decode_read_flush(h, *[a[n] for n in names], None)
+
+    assert call(y=None) == 1
+    assert call(q=None) == 1
+    assert call(frames=None) == 1     # sketch heads need their maps
+    assert call(beta=FAKE) == 1       # Mamba-2 takes no beta
+    assert call(kbuf=None) == 1       # the window is read
+    assert call(y=FAKE + 4) == 3      # misaligned
+    assert L.sketchssm_decode_read_flush(None, *([None] * 14), None) == 1
+
+
 def test_shared_key_heads_accepted():
     for kq in (0, 1, 2, 4, 8):
         B.Plan(_shape(kq=kq), np.full(8, 3, np.int32), np.repeat(np.arange(2, dtype=np.int32), 4))

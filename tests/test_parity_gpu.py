@@ -47,7 +47,8 @@ def _slab_err(got, ref):
 class Run:
     """Drive one layer on the GPU and the oracle on a set of (b, h) items."""
 
-    def __init__(self, wl, items=None, dense_baseline=False, step_source=None, z_error_bound=False):
+    def __init__(self, wl, items=None, dense_baseline=False, step_source=None, z_error_bound=False,
+                 fused=False):
         from rank_state_read_amd.layer import layer_for_workload
         self.wl = wl
         c = wl.cfg
@@ -69,6 +70,8 @@ class Run:
         # to the fp32 forward error bound of its K-term products, (K + 2) u
         # |Omega_r| |S| (u = 2^-24), where that exceeds 1e-4 of the slab.
         self.z_error_bound = z_error_bound
+        # fused: the window's last read and its flush in one call
+        self.fused = fused
 
     def init_sketch(self):
         self.lay.flush(0)
@@ -104,12 +107,15 @@ class Run:
         st = self.src.step(self.t)
         dev = self.lay.upload_step(st)
         pos = self.t % c.W
-        if self.dense:
-            y = self.lay.dense_read(pos, dev["q"], dev["k"], dev["v"], dev["a"], dev["beta"])
+        if self.fused and pos == c.W - 1:
+            y = self.lay.read_flush(dev["q"], dev["k"], dev["v"], dev["a"], dev["beta"])
         else:
-            y = self.lay.read(pos, dev["q"], dev["k"], dev["v"], dev["a"], dev["beta"])
-        if pos == c.W - 1:
-            self.lay.flush(c.W)
+            if self.dense:
+                y = self.lay.dense_read(pos, dev["q"], dev["k"], dev["v"], dev["a"], dev["beta"])
+            else:
+                y = self.lay.read(pos, dev["q"], dev["k"], dev["v"], dev["a"], dev["beta"])
+            if pos == c.W - 1:
+                self.lay.flush(c.W)
         so = gather_items(st, self.items)
         yo, _ = self.orc.read(so["q"], so["k"], so["v"], so["a"], so["beta"])
         torch.cuda.synchronize()
@@ -418,3 +424,49 @@ def test_fp32_qkv(kind, V):
     cfg = _edge_cfg(kind, V, qkv="f32")
     ranks = np.array([1, 16, 0, 17, 49, 6, 3, 0], np.int32)
     _run_steps(Workload(cfg, ranks=ranks), cfg.W + 5)
+
+
+
+# ---------------------------------------------------------------------------
+# the window's last read fused into its flush (sketchssm_decode_read_flush)
+# ---------------------------------------------------------------------------
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,B", [("c0", 2), ("c1", 20), ("c2", 20), ("c3", 37), ("c4", 37)])
+def test_fused_last_read(name, B):
+    wl = Workload(CONFIGS[name].with_batch(B))
+    _run_steps(wl, 2 * wl.cfg.W + 3, fused=True)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("kind,V,qkv", [("mamba2", 80, "bf16"), ("gdn", 128, "bf16"), ("kda", 128, "bf16"),
+                                        ("mamba2", 64, "f32"), ("gdn", 80, "f32"), ("kda", 64, "f32")])
+def test_fused_last_read_rank_extremes(kind, V, qkv):
+    """Map tiles beyond the first (ranks 17 .. 64) and dense heads in the fused read."""
+    cfg = _edge_cfg(kind, V, cap=64, qkv=qkv)
+    ranks = np.array([1, 16, 0, 17, 64, 33, 49, 0], np.int32)
+    _run_steps(Workload(cfg, ranks=ranks), 2 * cfg.W + 3, fused=True)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,kq", [("c1", 8), ("c4", 16)])
+def test_fused_last_read_shared_keys(name, kq):
+    import dataclasses
+    cfg = dataclasses.replace(CONFIGS[name].with_batch(19), kq_heads=kq)
+    _run_steps(Workload(cfg), cfg.W + 5, fused=True)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,B", [("c1", 20), ("c3", 19), ("c4", 19)])
+def test_fused_last_read_dense_baseline(name, B):
+    cfg = CONFIGS[name].with_batch(B)
+    wl = Workload(cfg)
+    wl0 = Workload(cfg, ranks=np.zeros(cfg.H, np.int32), basis=wl.basis)
+    _run_steps(wl0, cfg.W + 3, dense_baseline=True, step_source=wl, fused=True)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["c1", "c4"])
+def test_fused_last_read_full_size_sampled(name):
+    cfg = CONFIGS[name].with_steps(CONFIGS[name].W + 2)
+    wl = Workload(cfg)
+    _run_steps(wl, cfg.steps, items=_sample_items(wl), fused=True)
