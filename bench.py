@@ -180,7 +180,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
-    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=256)
     ap.add_argument("--config", default="c1")
     ap.add_argument("--instances", type=int, default=4,
                     help="independent layer instances the steps rotate over")
