@@ -1,7 +1,8 @@
 """The launch path allocates nothing and never synchronises, so a whole window
-of decode reads and its flush can be captured in a HIP graph.  Each replay,
-from the same starting state, must reproduce the eager run bit for bit; eager
-work and host synchronisations sit between the replays."""
+of decode reads and its flush can be captured in a HIP graph, with the window's
+last read either apart or fused into the flush.  Each replay, from the same
+starting state, must reproduce the eager run bit for bit; eager work and host
+synchronisations sit between the replays."""
 import numpy as np
 import pytest
 
@@ -21,8 +22,9 @@ def _need_gpu():
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("name,B", [("c1", 20), ("c4", 19)])
-def test_window_replays_match_eager(name, B):
+@pytest.mark.parametrize("fused", [False, True], ids=["apart", "fused"])
+@pytest.mark.parametrize("name,B", [("c1", 20), ("c3", 23), ("c4", 19)])
+def test_window_replays_match_eager(name, B, fused):
     from rank_state_read_amd.layer import layer_for_workload
     cfg = CONFIGS[name].with_batch(B)
     wl = Workload(cfg)
@@ -33,10 +35,14 @@ def test_window_replays_match_eager(name, B):
     start = (lay.S.clone(), lay.Z.clone())
 
     def window():
-        for pos in range(cfg.W):
+        for pos in range(cfg.W - 1 if fused else cfg.W):
             d = inputs[pos]
             lay.read(pos, d["q"], d["k"], d["v"], d["a"], d["beta"], y=ys[pos])
-        lay.flush(cfg.W)
+        if fused:
+            d = inputs[cfg.W - 1]
+            lay.read_flush(d["q"], d["k"], d["v"], d["a"], d["beta"], y=ys[cfg.W - 1])
+        else:
+            lay.flush(cfg.W)
 
     def restore():
         lay.S.copy_(start[0])
@@ -65,5 +71,6 @@ def test_window_replays_match_eager(name, B):
         d = inputs[0]
         lay.read(0, d["q"], d["k"], d["v"], d["a"], d["beta"])
         torch.cuda.synchronize()
-    print(f"  {name} B={B}: 3 replays of {cfg.W} reads + flush match the eager run", flush=True)
+    how = "fused last read" if fused else "flush"
+    print(f"  {name} B={B}: 3 replays of the window's reads + {how} match the eager run", flush=True)
     assert np.isfinite(eager[1].cpu().numpy()).all()
