@@ -71,6 +71,8 @@ typedef enum {
     SKSSM_F32 = 1       /* q, k, v and the window's k, v in float32 */
 } sketchssm_dtype;
 
+/* One layer's state, B * H * K * V fp32 elements, must stay below 2^31 (8 GiB):
+ * up to 1638 sequences at 128 heads of 128 x 80.  Larger shapes give SKSSM_ESHAPE. */
 typedef struct {
     int32_t B;          /* batch (sequences) */
     int32_t H;          /* state heads of the layer */

@@ -69,6 +69,8 @@ def test_plan_hand_example_from_library(golden_dir):
 @pytest.mark.parametrize("bad", [
     dict(H=0), dict(H=257), dict(V=96), dict(G=0), dict(cap=65), dict(B_=0),
     dict(kq=3), dict(kq=16), dict(kq=-1),
+    # one layer's state must stay below 2^31 elements: 1639 x 128 x 128 x 80 is past it
+    dict(B_=1639, H=128, G=8),
 ])
 def test_plan_rejects_bad_shapes(bad):
     kw = dict(H=8, G=2)
@@ -77,6 +79,13 @@ def test_plan_rejects_bad_shapes(bad):
     with pytest.raises(B.SketchSSMError) as e:
         B.Plan(_shape(**kw), np.ones(H, np.int32), np.zeros(H, np.int32))
     assert e.value.status == 2
+
+
+def test_largest_state_is_accepted():
+    """1638 sequences of the Nano layer (128 heads, 128 x 80 state): 8.0 GiB of
+    state, the most one plan takes."""
+    p = B.Plan(_shape(B_=1638, H=128, G=8), np.ones(128, np.int32), np.repeat(np.arange(8), 16))
+    assert p.z_elems == 1638 * 80 * 128
 
 
 def test_plan_rejects_bad_tables():

@@ -48,14 +48,18 @@ class Run:
     """Drive one layer on the GPU and the oracle on a set of (b, h) items."""
 
     def __init__(self, wl, items=None, dense_baseline=False, step_source=None, z_error_bound=False,
-                 fused=False):
+                 fused=False, fill_state=None):
         from rank_state_read_amd.layer import layer_for_workload
         self.wl = wl
         c = wl.cfg
         self.cfg = c
         self.dense = dense_baseline
         self.src = step_source or wl
-        self.lay = layer_for_workload(wl)
+        # fill_state(S): writes the initial state into the device tensor instead
+        # of the workload's own draw
+        self.lay = layer_for_workload(wl, with_state=fill_state is None)
+        if fill_state is not None:
+            fill_state(self.lay.S)
         self.items = items if items is not None else [(b, h) for b in range(c.B) for h in range(c.H)]
         S0 = np.stack([self.lay.S[b, h].cpu().numpy() for (b, h) in self.items]) \
             if len(self.items) < c.B * c.H else self.lay.S.cpu().numpy().reshape(-1, c.K, c.V)
@@ -462,6 +466,56 @@ def test_fused_last_read_dense_baseline(name, B):
     wl = Workload(cfg)
     wl0 = Workload(cfg, ranks=np.zeros(cfg.H, np.int32), basis=wl.basis)
     _run_steps(wl0, cfg.W + 3, dense_baseline=True, step_source=wl, fused=True)
+
+
+class _TiledRows:
+    """Inputs for a large batch drawn cheaply from a small one: row b takes the
+    tokens of row b % P of the small workload, with q and v scaled by a power of
+    two that changes every P rows (exact in bf16).  Together with a state that
+    differs in every row, each row's outputs are its own."""
+
+    def __init__(self, small, B):
+        self.small = small
+        self.P = small.cfg.B
+        self.idx = np.arange(B) % self.P
+        self.scale = 2.0 ** ((np.arange(B) // self.P) % 5 - 2)
+
+    def step(self, t):
+        from workloads import to_bf16_bits
+        st = self.small.step(t)
+        out = {}
+        for key, val in st.items():
+            if val is None or key.endswith("_bits"):
+                continue
+            x = val[self.idx]
+            if key in ("q", "v"):
+                x = (x * self.scale.reshape((-1,) + (1,) * (x.ndim - 1))).astype(val.dtype)
+            out[key] = x
+            if st.get(key + "_bits") is not None:
+                out[key + "_bits"] = to_bf16_bits(x.astype(np.float32))
+        out.setdefault("beta", None)
+        return out
+
+
+@pytest.mark.timeout(600)
+def test_fused_last_read_largest_batch():
+    """The Nano layer at 1638 sequences, the largest state one plan takes (8.6 GB;
+    offsets past 2^32 bytes, 209 664 flush blocks): a window of reads with the
+    last one fused into its flush, checked on sampled rows across the batch."""
+    cfg = CONFIGS["c1"].with_batch(1638).with_steps(CONFIGS["c1"].W + 2)
+    wl = Workload(cfg)
+    P = 23
+    small = Workload(CONFIGS["c1"].with_batch(P))
+    base = torch.from_numpy(np.stack([small.state_batch(b) for b in range(P)])).cuda()
+
+    def fill(S):
+        for b in range(cfg.B):
+            S[b].copy_(base[b % P] * (1.0 + b / 2048.0))
+
+    items = _sample_items(wl) + [(b, h) for b in (P, 2 * P + 1, cfg.B // 2, cfg.B - 2) for h in (0, 63, 127)]
+    items = sorted(set(items))
+    _log(f"  c1 at B={cfg.B}: {len(items)} sampled items")
+    _run_steps(wl, cfg.steps, items=items, fused=True, step_source=_TiledRows(small, cfg.B), fill_state=fill)
 
 
 @pytest.mark.timeout(600)
