@@ -498,23 +498,26 @@ class _TiledRows:
 
 
 @pytest.mark.timeout(600)
-def test_fused_last_read_largest_batch():
-    """The Nano layer at 1638 sequences, the largest state one plan takes (8.6 GB;
-    offsets past 2^32 bytes, 209 664 flush blocks): a window of reads with the
-    last one fused into its flush, checked on sampled rows across the batch."""
-    cfg = CONFIGS["c1"].with_batch(1638).with_steps(CONFIGS["c1"].W + 2)
+@pytest.mark.parametrize("name,B", [("c1", 1638), ("c3", 4095), ("c4", 4095)])
+def test_fused_last_read_largest_batch(name, B):
+    """Each layer at the largest batch one plan takes (B H K V just below 2^31
+    elements, 8.6 GB of state; offsets past 2^32 bytes, up to 209 664 flush
+    blocks): a window of reads with the last one fused into its flush, checked
+    on sampled rows across the batch."""
+    cfg = CONFIGS[name].with_batch(B).with_steps(CONFIGS[name].W + 2)
     wl = Workload(cfg)
     P = 23
-    small = Workload(CONFIGS["c1"].with_batch(P))
+    small = Workload(CONFIGS[name].with_batch(P))
     base = torch.from_numpy(np.stack([small.state_batch(b) for b in range(P)])).cuda()
 
     def fill(S):
         for b in range(cfg.B):
             S[b].copy_(base[b % P] * (1.0 + b / 2048.0))
 
-    items = _sample_items(wl) + [(b, h) for b in (P, 2 * P + 1, cfg.B // 2, cfg.B - 2) for h in (0, 63, 127)]
+    items = _sample_items(wl) + [(b, h) for b in (P, 2 * P + 1, cfg.B // 2, cfg.B - 2)
+                                 for h in (0, cfg.H // 2, cfg.H - 1)]
     items = sorted(set(items))
-    _log(f"  c1 at B={cfg.B}: {len(items)} sampled items")
+    _log(f"  {name} at B={cfg.B}: {len(items)} sampled items")
     _run_steps(wl, cfg.steps, items=items, fused=True, step_source=_TiledRows(small, cfg.B), fill_state=fill)
 
 
