@@ -28,8 +28,10 @@
 // operand -(T (gamma K)) and the 16 x V tile T V_w.  Once the state has landed
 // each wave only runs MFMAs on its own columns -- U (kept in registers, where
 // its accumulator layout is already the B operand of the update), the update,
-// Z, then the store -- with no barrier unless the head's rank exceeds 16 (each
-// further 16-row basis tile is staged between two barriers).
+// Z -- with no barrier unless the head's rank exceeds 16 (each further 16-row
+// basis tile is staged between two barriers).  The Mamba-2 kernels then store
+// the state as whole rows staged through LDS; the delta-rule ones store it
+// from the accumulator layout.
 //
 // The state tiles serve directly as the B operand of the products with S: the
 // register index r of a tile is used as the 4-wide K step, which only permutes
@@ -41,6 +43,7 @@
 
 #include "device_common.h"
 #include "sketchssm_internal.h"
+#include "state_tiles.h"
 
 namespace skssm {
 
@@ -642,10 +645,19 @@ void flush_kernel(FlushArgs A, HeadTable T) {
     };
     if (n > 0) {
         if (sketch) sketch_rows();
+        if (DELTA) {
+            // staging the state through LDS measured no faster for the
+            // delta-rule kernels (eight waves, three blocks per CU)
 #pragma unroll
-        for (int kt = 0; kt < 8; ++kt)
+            for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) buffer_store_f32(s[kt][rr], srs, svo, (16 * kt + rr) * V * 4);
+                for (int rr = 0; rr < 4; ++rr) buffer_store_f32(s[kt][rr], srs, svo, (16 * kt + rr) * V * 4);
+        } else {
+            // whole rows through the window-phase LDS (keys and values), dead
+            // once every wave has applied the update
+            static_assert(2 * 16 * VS <= L::om, "state tiles overlap the basis tile");
+            store_state_tiles<V>(s, sm, srs, tid);
+        }
     } else if (sketch) {
         __syncthreads();
         sketch_rows();

@@ -9,16 +9,18 @@
 //
 // One block per item with V/16 waves.  Wave w holds value columns 16w..16w+15
 // for all 128 key rows in registers (lane l, register (kt, r) <-> key row
-// 16 kt + 4 (l/16) + r, column 16 w + l % 16), loaded and stored with buffer
+// 16 kt + 4 (l/16) + r, column 16 w + l % 16), loaded with buffer
 // instructions.  Both sums over keys (the erase term k^T S and the output
 // S^T q) are a per-lane sum over the lane's 32 rows plus two exchanges between
-// quarter-waves, so after the token is staged in LDS no barrier is needed.
+// quarter-waves, so after the token is staged in LDS no barrier is needed
+// until the updated state leaves as whole rows staged through LDS.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
 
 #include "device_common.h"
 #include "sketchssm_internal.h"
+#include "state_tiles.h"
 
 namespace skssm {
 
@@ -59,6 +61,7 @@ void rmw_kernel(RmwArgs A) {
     __shared__ __align__(16) float qs[K];
     __shared__ __align__(16) float ks[K];
     __shared__ __align__(16) float als[KDA ? K : 4];
+    __shared__ __align__(16) float st[2 * 16 * (V + 4)];  // the state on its way out
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -128,10 +131,7 @@ void rmw_kernel(RmwArgs A) {
     }
     yc = quarter_sum(yc);
     if (lq == 0) A.y[item * V + v0 + lr] = yc;
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) buffer_store_f32(s[kt][rr], srs, svo, (16 * kt + rr) * V * 4);
+    store_state_tiles<V>(s, st, srs, tid);
 }
 
 template <int KIND, int V, typename QT>
