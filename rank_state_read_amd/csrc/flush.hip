@@ -182,6 +182,9 @@ void flush_kernel(FlushArgs A, HeadTable T) {
     const int g = __builtin_amdgcn_readfirstlane(T.group[p]);
     const size_t item = size_t(b) * A.H + h;
     const bool sketch = r > 0 && A.Z != nullptr;
+    // no tokens and no sketch to emit (a dense head's initial sketch): the
+    // state stays as it is and the block has nothing to read
+    if (n == 0 && !sketch) return;
     const int v0 = 16 * w;
     // window slot i of this item: [W][H][B] layout, slot-major (keys: [W][Hk][B])
     auto wslot = [&](int i) { return (size_t(i) * A.H + h) * A.B + b; };
