@@ -414,6 +414,20 @@ def test_degenerate_tokens(kind, V):
 
 
 @pytest.mark.timeout(300)
+@pytest.mark.parametrize("kind,V", [("mamba2", 80), ("gdn", 128), ("kda", 64)])
+@pytest.mark.parametrize("B", [16, 17])
+def test_single_head(kind, V, B):
+    """A layer of one head: exactly one 16-row tile, or one and a ragged row;
+    as a sketch head and as a dense head, with the window's last read apart
+    from its flush and fused into it."""
+    cfg = Config(f"edge-h1-{kind}", kind, B=B, H=1, K=128, V=V, G=1, W=16, steps=20, qkv="bf16",
+                 mean_rank=7, rank_cap=49, n_dense=0, seed=79)
+    for r in (7, 0):
+        for fused in (False, True):
+            _run_steps(Workload(cfg, ranks=np.array([r], np.int32)), cfg.W + 2, fused=fused)
+
+
+@pytest.mark.timeout(300)
 def test_max_heads():
     """256 heads (the largest the head table indexes), dense heads among them."""
     cfg = Config("edge-h256", "mamba2", B=3, H=256, K=128, V=64, G=16, W=16, steps=20, qkv="bf16",
