@@ -2,6 +2,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1] [--no-cpu]
 
+K is rounded up to whole periods of the step loop (instances x 16 steps, 64 by
+default) so that every window position and the flush weigh the same.
+
 A step is one decode step of one layer: the read of every (b, h) item at the
 current window position, plus the flush (apply the 16 buffered tokens, emit the
 sketch) after every 16th read.  Steps rotate over several independent layer
@@ -303,6 +306,10 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
+    # the timed steps cover whole periods (every layer instance through a whole
+    # window), so that every window position and the flush weigh the same in the
+    # mean: --steps is rounded up to a multiple of instances x W, and "steps" in
+    # the output line is the number actually timed
     period = NI * W
     K = max(period, (args.steps + period - 1) // period * period)
     warm = max(0, args.warmup)
@@ -435,6 +442,7 @@ def main():
         "unit": "us per layer decode step",
         "n_gpus": 1,
         "steps": K,
+        "steps_requested": args.steps,
         "warmup": warm,
         "ms_per_step": round(us_step / 1000.0, 6),
         "higher_is_better": False,
