@@ -30,8 +30,8 @@
 // its accumulator layout is already the B operand of the update), the update,
 // Z -- with no barrier unless the head's rank exceeds 16 (each further 16-row
 // basis tile is staged between two barriers).  The Mamba-2 kernels then store
-// the state as whole rows staged through LDS; the delta-rule ones store it
-// from the accumulator layout.
+// the sketch rows and the state as whole rows staged through LDS; the
+// delta-rule ones store them from the accumulator layout.
 //
 // The state tiles serve directly as the B operand of the products with S: the
 // register index r of a tile is used as the 4-wide K step, which only permutes
@@ -639,10 +639,24 @@ void flush_kernel(FlushArgs A, HeadTable T) {
 #pragma unroll
                 for (int ss = 0; ss < 4; ++ss) z = mfma_16x16x4(o[ss], s[kt][ss], z);
             }
+            if (DELTA) {
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const int m = 16 * mt + 4 * lq + rr;
-                if (m < r) Zi[size_t(m) * V + v0 + lr] = z[rr];
+                for (int rr = 0; rr < 4; ++rr) {
+                    const int m = 16 * mt + 4 * lq + rr;
+                    if (m < r) Zi[size_t(m) * V + v0 + lr] = z[rr];
+                }
+            } else {
+                // whole sketch rows through the dead window-phase LDS, as the state
+                static_assert(16 * VS <= L::om, "sketch tile overlaps the basis tile");
+                __syncthreads();  // every wave is past the update and the last tile's reads
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) sm[(4 * lq + rr) * VS + v0 + lr] = z[rr];
+                __syncthreads();
+                const int rows = min(16, r - 16 * mt);
+                const int row = tid / (V / 4), c4 = tid - row * (V / 4);  // 4 V threads: one piece each
+                if (row < rows)
+                    *reinterpret_cast<float4*>(Zi + size_t(16 * mt + row) * V + 4 * c4) =
+                        *reinterpret_cast<const float4*>(sm + row * VS + 4 * c4);
             }
         }
     };
