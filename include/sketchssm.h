@@ -135,7 +135,8 @@ size_t sketchssm_frame_elems(const sketchssm_plan* plan);
  * over S, write the sketch Z = Omega_r S of every sketch head (Abstract: S is
  * read a single time per update and its products with the basis are stored).
  *   S      device [B,H,K,V] fp32, in/out.  n_tokens = 0 leaves S bitwise
- *          unchanged and only writes Z (the initial sketch after prefill).
+ *          unchanged and only writes Z (the initial sketch after prefill);
+ *          dense heads' states are then not even read.
  *   Z      device [sketchssm_z_elems] fp32, out; may be NULL when no head has a rank
  *   basis  device [G, basis_rows, K] fp32
  *   kbuf   device [W,Hk,B,K] of the qkv dtype     (window keys)
