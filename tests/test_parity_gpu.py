@@ -19,6 +19,7 @@ pytestmark = pytest.mark.gpu
 
 from oracle import gather_items, items_oracle  # noqa: E402
 from workloads import CONFIGS, Config, Workload  # noqa: E402
+from tiled_inputs import TiledRows, tiled_state_fill  # noqa: E402
 
 TOL = 1e-4
 
@@ -482,35 +483,6 @@ def test_fused_last_read_dense_baseline(name, B):
     _run_steps(wl0, cfg.W + 3, dense_baseline=True, step_source=wl, fused=True)
 
 
-class _TiledRows:
-    """Inputs for a large batch drawn cheaply from a small one: row b takes the
-    tokens of row b % P of the small workload, with q and v scaled by a power of
-    two that changes every P rows (exact in bf16).  Together with a state that
-    differs in every row, each row's outputs are its own."""
-
-    def __init__(self, small, B):
-        self.small = small
-        self.P = small.cfg.B
-        self.idx = np.arange(B) % self.P
-        self.scale = 2.0 ** ((np.arange(B) // self.P) % 5 - 2)
-
-    def step(self, t):
-        from workloads import to_bf16_bits
-        st = self.small.step(t)
-        out = {}
-        for key, val in st.items():
-            if val is None or key.endswith("_bits"):
-                continue
-            x = val[self.idx]
-            if key in ("q", "v"):
-                x = (x * self.scale.reshape((-1,) + (1,) * (x.ndim - 1))).astype(val.dtype)
-            out[key] = x
-            if st.get(key + "_bits") is not None:
-                out[key + "_bits"] = to_bf16_bits(x.astype(np.float32))
-        out.setdefault("beta", None)
-        return out
-
-
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name,B", [("c1", 1638), ("c3", 4095), ("c4", 4095)])
 def test_fused_last_read_largest_batch(name, B):
@@ -522,17 +494,13 @@ def test_fused_last_read_largest_batch(name, B):
     wl = Workload(cfg)
     P = 23
     small = Workload(CONFIGS[name].with_batch(P))
-    base = torch.from_numpy(np.stack([small.state_batch(b) for b in range(P)])).cuda()
-
-    def fill(S):
-        for b in range(cfg.B):
-            S[b].copy_(base[b % P] * (1.0 + b / 2048.0))
+    fill = tiled_state_fill(small, cfg.B)
 
     items = _sample_items(wl) + [(b, h) for b in (P, 2 * P + 1, cfg.B // 2, cfg.B - 2)
                                  for h in (0, cfg.H // 2, cfg.H - 1)]
     items = sorted(set(items))
     _log(f"  {name} at B={cfg.B}: {len(items)} sampled items")
-    _run_steps(wl, cfg.steps, items=items, fused=True, step_source=_TiledRows(small, cfg.B), fill_state=fill)
+    _run_steps(wl, cfg.steps, items=items, fused=True, step_source=TiledRows(small, cfg.B), fill_state=fill)
 
 
 @pytest.mark.timeout(600)

@@ -34,10 +34,13 @@ def _slab_err(got, ref):
     return float((np.abs(got - ref).max(axis=1) / den).max())
 
 
-def _run(wl, steps, items=None):
+def _run(wl, steps, items=None, step_source=None, fill_state=None):
     from rank_state_read_amd.layer import layer_for_workload
     c = wl.cfg
-    lay = layer_for_workload(wl)
+    lay = layer_for_workload(wl, with_state=fill_state is None)
+    if fill_state is not None:
+        fill_state(lay.S)
+    src = step_source or wl
     items = items if items is not None else [(b, h) for b in range(c.B) for h in range(c.H)]
     bi = torch.as_tensor([b for b, _ in items])
     hi = torch.as_tensor([h for _, h in items])
@@ -46,7 +49,7 @@ def _run(wl, steps, items=None):
     worst = 0.0
     t0 = time.time()
     for t in range(steps):
-        st = wl.step(t)
+        st = src.step(t)
         dev = lay.upload_step(st)
         y = lay.rmw_step(dev["q"], dev["k"], dev["v"], dev["a"], dev["beta"])
         so = gather_items(st, items)
@@ -96,3 +99,17 @@ def test_rmw_widths_and_dtypes(kind, V, qkv):
     cfg = Config(f"rmw-{kind}-{V}-{qkv}", kind, B=19, H=8, K=128, V=V, G=2, W=16, steps=20, qkv=qkv,
                  mean_rank=6, rank_cap=49, n_dense=0, seed=79)
     _run(Workload(cfg), 20)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,B", [("c1", 1638), ("c4", 4095)])
+def test_rmw_largest_batch(name, B):
+    """The largest batch a shape takes (8.6 GB of state), sampled rows across it."""
+    from tiled_inputs import TiledRows, tiled_state_fill
+    wl = Workload(CONFIGS[name].with_batch(B))
+    c = wl.cfg
+    small = Workload(CONFIGS[name].with_batch(23))
+    rng = np.random.default_rng(c.seed + 11)
+    items = sorted({(0, 0), (B - 1, c.H - 1), (B // 2, c.H // 2)} |
+                   {(int(rng.integers(B)), int(rng.integers(c.H))) for _ in range(30)})
+    _run(wl, 6, items=items, step_source=TiledRows(small, B), fill_state=tiled_state_fill(small, B))
