@@ -119,3 +119,22 @@ def test_shared_keys_gather_to_their_heads():
         for key in ("q", "k", "v", "a"):
             assert np.array_equal(g[key][i], one[key]), (key, b, h)
         assert np.array_equal(g["k"][i], st["k"][b, h // 16])
+
+
+def test_tiled_rows_for_large_batches():
+    """The large-batch inputs of the largest-batch GPU tests: row b repeats row
+    b % P with q and v scaled by an exact power of two, and the bf16 bits agree
+    with the values."""
+    from tiled_inputs import TiledRows
+    small = Workload(CONFIGS["c1"].with_batch(23))
+    tr = TiledRows(small, 130)
+    st, s0 = tr.step(3), small.step(3)
+    for key in ("q", "k", "v"):
+        assert np.array_equal(bf16_bits_to_f32(st[key + "_bits"]), st[key]), key
+    for b in (0, 22, 23, 77, 129):
+        scale = 2.0 ** ((b // 23) % 5 - 2)
+        assert np.array_equal(st["k"][b], s0["k"][b % 23])
+        assert np.array_equal(st["a"][b], s0["a"][b % 23])
+        assert np.array_equal(st["q"][b], s0["q"][b % 23] * scale)
+        assert np.array_equal(st["v"][b], s0["v"][b % 23] * scale)
+    assert st["beta"] is None
