@@ -8,8 +8,8 @@
  * "SketchSSM: Write to the Full State, Read from a Compact Sketch", Abstract).
  *
  * Per (batch b, head h) "item" with key dim K and value dim V:
- *   state     S in R^{K x V}, fp32 ("--mamba-ssm-cache-dtype float32" on the
- *             PyPI page, "Quick start: serve with vLLM");
+ *   state     S in R^{K x V}, fp32 (the PyPI page's serving command keeps the
+ *             recurrent state cache in float32, "Quick start: serve with vLLM");
  *   basis     Omega_g in R^{basis_rows x K}, one per head group; a head of rank
  *             r uses its first r rows (calibration card "SketchSSM calibration:
  *             Nemotron Nano 9B v2", "Contents": basis (27, 8, 79, 128));
@@ -93,8 +93,10 @@ typedef struct sketchssm_plan sketchssm_plan;   /* opaque, immutable once made *
 
 /*
  * Host only (no HIP call).  Checks the shape and the rank table and derives the
- * frames and the launch order ("per-head rank table" and "ordered frames for
- * any mean rank are derived", calibration card, opening paragraph).
+ * frames and the launch order (the calibration card obtains each head's rank
+ * and the frame order from its allocation scores for whatever mean rank is
+ * asked for; card "SketchSSM calibration: Nemotron Nano 9B v2", opening
+ * paragraph).
  *   rank[H]  : 0 = dense fallback, else 1 <= rank <= min(rank_cap, basis_rows, K)
  *   group[H] : basis group of each head, 0 <= group < G
  * Frames are the distinct (group, rank) pairs of the sketch heads sorted by

@@ -10,7 +10,6 @@ from .sketchssm_oracle import (  # noqa: F401
     gather_items,
     items_oracle,
     plan,
-    run_window,
     transition,
     write_weight,
 )

@@ -74,9 +74,10 @@ def plan(rank: Sequence[int], group: Sequence[int], G: int, K: int,
          basis_rows: int, rank_cap: int) -> Dict[str, object]:
     """Frames and launch order derived from a per-head rank table.
 
-    The calibration card says per-head rank tables and *ordered frames* are
-    derived from the calibration for any mean rank ("SketchSSM calibration:
-    Nemotron Nano 9B v2", opening paragraph and "Verified mean ranks").  The
+    On the calibration card, a head's rank and the order of the frames are
+    obtained from the calibration for whatever mean rank is asked for
+    ("SketchSSM calibration: Nemotron Nano 9B v2", opening paragraph and
+    "Verified mean ranks").  The
     pages do not define the order, so this rule is ours:
 
     * a frame is one (group, rank) coefficient map; frames are the distinct
@@ -325,14 +326,3 @@ def gather_items(step: dict, items: Sequence[tuple]) -> dict:
         else:
             out[key] = x[bi, hi]
     return out
-
-
-def run_window(orc: BatchOracle, steps: List[dict]) -> np.ndarray:
-    """Read each step's token (flushing after every W-th read); returns y [T, n, V]."""
-    ys = []
-    for st in steps:
-        y, _ = orc.read(st["q"], st["k"], st["v"], st["a"], st.get("beta"))
-        ys.append(y)
-        if orc.j == orc.W:
-            orc.flush()
-    return np.stack(ys)

@@ -2,12 +2,13 @@
 // the launch order from a per-head rank table.  Plain C++, no HIP calls, so it
 // runs (and is tested) on machines without a GPU.
 //
-// The calibration card ("SketchSSM calibration: Nemotron Nano 9B v2", opening
-// paragraph) says the per-head rank table and the ordered frames for any mean
-// rank are derived from the calibration; the PyPI page ("Make a calibration for
-// your model", allocate stage) gives each head a rank or a dense fallback, and
-// the card caps ranks ("Contents": allocation rank cap 49).  The pages do not
-// define the frame order or any scheduling; the rule here is this library's:
+// On the calibration card ("SketchSSM calibration: Nemotron Nano 9B v2", opening
+// paragraph) each head's rank and the order of the frames come out of the
+// calibration's allocation scores for whatever mean rank is requested; the
+// PyPI page ("Make a calibration for your model", allocate stage) gives each
+// head a rank or a dense fallback, and the card caps ranks ("Contents":
+// allocation rank cap 49).  The pages do not define the frame order or any
+// scheduling; the rule here is this library's:
 //   frames  = distinct (group, rank) of sketch heads, sorted by group then rank
 //   bucket  = 0 for dense, else 1 + (rank - 1) / 8
 //   order   = dense heads, then buckets high to low, head ascending inside one.

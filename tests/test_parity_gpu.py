@@ -6,10 +6,6 @@ per slab, max |gpu - ref| / max |ref|, where a slab is one (t, b, h) output
 vector, one item's K x V state or one item's r x V sketch; integer tables are
 compared bit for bit in the CPU tests.
 """
-import os
-import sys
-import time
-
 import numpy as np
 import pytest
 
@@ -20,13 +16,7 @@ pytestmark = pytest.mark.gpu
 from oracle import gather_items, items_oracle  # noqa: E402
 from workloads import CONFIGS, Config, Workload  # noqa: E402
 from tiled_inputs import TiledRows, tiled_state_fill  # noqa: E402
-
-TOL = 1e-4
-
-
-def _log(msg):
-    print(msg, flush=True)
-    sys.stdout.flush()
+from parity_run import TOL, Run, _log, _run_steps, _sample_items, _slab_err  # noqa: E402
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -35,116 +25,6 @@ def _need_gpu():
         pytest.skip("no GPU")
     from rank_state_read_amd import binding
     binding.lib()
-
-
-def _slab_err(got, ref):
-    """max over slabs of max|got-ref| / max|ref|; slabs along the leading axis."""
-    got = np.asarray(got, np.float64).reshape(len(ref), -1)
-    ref = np.asarray(ref, np.float64).reshape(len(ref), -1)
-    den = np.maximum(np.abs(ref).max(axis=1), 1e-30)
-    return float((np.abs(got - ref).max(axis=1) / den).max())
-
-
-class Run:
-    """Drive one layer on the GPU and the oracle on a set of (b, h) items."""
-
-    def __init__(self, wl, items=None, dense_baseline=False, step_source=None, z_error_bound=False,
-                 fused=False, fill_state=None):
-        from rank_state_read_amd.layer import layer_for_workload
-        self.wl = wl
-        c = wl.cfg
-        self.cfg = c
-        self.dense = dense_baseline
-        self.src = step_source or wl
-        # fill_state(S): writes the initial state into the device tensor instead
-        # of the workload's own draw
-        self.lay = layer_for_workload(wl, with_state=fill_state is None)
-        if fill_state is not None:
-            fill_state(self.lay.S)
-        self.items = items if items is not None else [(b, h) for b in range(c.B) for h in range(c.H)]
-        S0 = np.stack([self.lay.S[b, h].cpu().numpy() for (b, h) in self.items]) \
-            if len(self.items) < c.B * c.H else self.lay.S.cpu().numpy().reshape(-1, c.K, c.V)
-        self.orc = items_oracle(wl, self.items, S_init=S0)
-        self.bi = np.array([b for b, _ in self.items])
-        self.hi = np.array([h for _, h in self.items])
-        self.sketch_items = [i for i, (b, h) in enumerate(self.items) if wl.ranks[h] > 0]
-        self.t = 0
-        self.max_err = {"y": 0.0, "S": 0.0, "Z": 0.0}
-        # With z_error_bound, a sketch whose rows cancel (basis rows nearly
-        # orthogonal to a low-rank state, |Omega_r S| << |Omega_r| |S|) is held
-        # to the fp32 forward error bound of its K-term products, (K + 2) u
-        # |Omega_r| |S| (u = 2^-24), where that exceeds 1e-4 of the slab.
-        self.z_error_bound = z_error_bound
-        # fused: the window's last read and its flush in one call
-        self.fused = fused
-
-    def init_sketch(self):
-        self.lay.flush(0)
-        torch.cuda.synchronize()
-        self.check_Z()
-
-    def check_S(self):
-        S = self.lay.S[torch.as_tensor(self.bi), torch.as_tensor(self.hi)].cpu().numpy()
-        e = _slab_err(S, self.orc.S0)
-        self.max_err["S"] = max(self.max_err["S"], e)
-        assert e <= TOL, f"S after flush at t={self.t}: {e:.3e}"
-
-    def check_Z(self):
-        if not self.sketch_items:
-            return
-        e = 0.0
-        for i in self.sketch_items:
-            b, h = self.items[i]
-            r = int(self.wl.ranks[h])
-            g = self.lay.z_item(b, h).cpu().numpy().astype(np.float64)
-            rr = self.orc.Z[i, :r]
-            den = max(np.abs(rr).max(), 1e-30)
-            if self.z_error_bound:
-                om = np.abs(self.wl.basis[int(self.wl.groups[h]), :r].astype(np.float64))
-                bound = (self.cfg.K + 2) * 2.0 ** -24 * (om @ np.abs(self.orc.S0[i])).max()
-                den = max(den, bound / TOL)
-            e = max(e, float(np.abs(g - rr).max() / den))
-        self.max_err["Z"] = max(self.max_err["Z"], e)
-        assert e <= TOL, f"Z at t={self.t}: {e:.3e}"
-
-    def step(self, check=True):
-        c = self.cfg
-        st = self.src.step(self.t)
-        dev = self.lay.upload_step(st)
-        pos = self.t % c.W
-        if self.fused and pos == c.W - 1:
-            y = self.lay.read_flush(dev["q"], dev["k"], dev["v"], dev["a"], dev["beta"])
-        else:
-            if self.dense:
-                y = self.lay.dense_read(pos, dev["q"], dev["k"], dev["v"], dev["a"], dev["beta"])
-            else:
-                y = self.lay.read(pos, dev["q"], dev["k"], dev["v"], dev["a"], dev["beta"])
-            if pos == c.W - 1:
-                self.lay.flush(c.W)
-        so = gather_items(st, self.items)
-        yo, _ = self.orc.read(so["q"], so["k"], so["v"], so["a"], so["beta"])
-        torch.cuda.synchronize()
-        self.t += 1
-        if check:
-            yg = y[torch.as_tensor(self.bi), torch.as_tensor(self.hi)].cpu().numpy()
-            e = _slab_err(yg, yo)
-            self.max_err["y"] = max(self.max_err["y"], e)
-            assert e <= TOL, f"y at t={self.t - 1} (pos {pos}): {e:.3e}"
-        if self.orc.j == c.W:
-            self.orc.flush()
-            if check:
-                self.check_S()
-                self.check_Z()
-
-
-def _run_steps(wl, steps, **kw):
-    r = Run(wl, **kw)
-    r.init_sketch()
-    t0 = time.time()
-    for _ in range(steps):
-        r.step()
-    _log(f"  {wl.cfg.name} B={wl.cfg.B} steps={steps} max errors {r.max_err} ({time.time() - t0:.1f}s)")
-    return r
 
 
 # ---------------------------------------------------------------------------
@@ -196,24 +76,6 @@ def test_long_run_drift(name):
 # ---------------------------------------------------------------------------
 # full sizes, in the launch configuration the benchmark times, sampled items
 # ---------------------------------------------------------------------------
-def _sample_items(wl):
-    c = wl.cfg
-    items = []
-    seen = set()
-    for h in range(c.H):
-        r = int(wl.ranks[h])
-        key = ("d", h) if r == 0 else (int(wl.groups[h]), r)
-        if key in seen:
-            continue
-        seen.add(key)
-        for b in (0, c.B - 1):
-            items.append((b, h))
-    rng = np.random.default_rng(c.seed)
-    for _ in range(16):
-        items.append((int(rng.integers(c.B)), int(rng.integers(c.H))))
-    return sorted(set(items))
-
-
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
 def test_full_size_sampled(name):
@@ -489,7 +351,11 @@ def test_fused_last_read_largest_batch(name, B):
     """Each layer at the largest batch one plan takes (B H K V just below 2^31
     elements, 8.6 GB of state; offsets past 2^32 bytes, up to 209 664 flush
     blocks): a window of reads with the last one fused into its flush, checked
-    on sampled rows across the batch."""
+    on sampled rows across the batch (inputs differ in every row, see
+    ``tiled_inputs``).  Afterwards the window slots that the last two reads
+    appended are read back at the sampled rows and compared bit for bit with
+    those tokens, so a slot address that lands on another row shows even where
+    the outputs would not."""
     cfg = CONFIGS[name].with_batch(B).with_steps(CONFIGS[name].W + 2)
     wl = Workload(cfg)
     P = 23
@@ -500,7 +366,30 @@ def test_fused_last_read_largest_batch(name, B):
                                  for h in (0, cfg.H // 2, cfg.H - 1)]
     items = sorted(set(items))
     _log(f"  {name} at B={cfg.B}: {len(items)} sampled items")
-    _run_steps(wl, cfg.steps, items=items, fused=True, step_source=TiledRows(small, cfg.B), fill_state=fill)
+    src = TiledRows(small, cfg.B)
+    r = _run_steps(wl, cfg.steps, items=items, fused=True, step_source=src, fill_state=fill)
+    _check_appended_slots(r, src, cfg.steps)
+
+
+def _check_appended_slots(r, src, steps):
+    """Window slots of the steps after the last flush, at the run's items,
+    bitwise against the tokens of those steps."""
+    W = r.cfg.W
+    first = (steps - 1) // W * W  # first step of the open window
+    bi, hi = torch.as_tensor(r.bi), torch.as_tensor(r.hi)
+    lay = r.lay
+    for t in range(first, steps):
+        slot = t - first
+        st = src.step(t)
+        for key, buf in (("k", lay.kbuf), ("v", lay.vbuf)):
+            got = buf[slot][hi, bi].cpu().view(torch.int16).numpy()
+            want = st[key + "_bits"][r.bi, r.hi].view(np.int16)
+            assert np.array_equal(got, want), f"window {key} slot {slot}"
+        got = lay.abuf[slot][hi, bi].cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), st["a"][r.bi, r.hi].view(np.uint32)), f"window decay slot {slot}"
+        if lay.bbuf is not None:
+            got = lay.bbuf[slot][hi, bi].cpu().numpy()
+            assert np.array_equal(got.view(np.uint32), st["beta"][r.bi, r.hi].view(np.uint32)), f"window beta slot {slot}"
 
 
 @pytest.mark.timeout(600)

@@ -122,19 +122,32 @@ def test_shared_keys_gather_to_their_heads():
 
 
 def test_tiled_rows_for_large_batches():
-    """The large-batch inputs of the largest-batch GPU tests: row b repeats row
-    b % P with q and v scaled by an exact power of two, and the bf16 bits agree
-    with the values."""
+    """The large-batch inputs of the largest-batch GPU tests: row b takes row
+    b % P of a small draw with heads rotated by s = b // P, the key's channels
+    rotated by (s // Hk) mod K, decays and betas scaled by 2^-((s // H) mod 8)
+    and q, v by 2^(((s // Hx) + s) mod 8 - 3); the bf16 bits agree with the
+    values, and no row repeats another at the largest batches."""
     from tiled_inputs import TiledRows
-    small = Workload(CONFIGS["c1"].with_batch(23))
-    tr = TiledRows(small, 130)
-    st, s0 = tr.step(3), small.step(3)
-    for key in ("q", "k", "v"):
-        assert np.array_equal(bf16_bits_to_f32(st[key + "_bits"]), st[key]), key
-    for b in (0, 22, 23, 77, 129):
-        scale = 2.0 ** ((b // 23) % 5 - 2)
-        assert np.array_equal(st["k"][b], s0["k"][b % 23])
-        assert np.array_equal(st["a"][b], s0["a"][b % 23])
-        assert np.array_equal(st["q"][b], s0["q"][b % 23] * scale)
-        assert np.array_equal(st["v"][b], s0["v"][b % 23] * scale)
-    assert st["beta"] is None
+    P = 23
+    for name, B, rows in (("c1", 130, (0, 22, 23, 77, 129)), ("c3", 4095, (0, 24, 736, 2944, 4094))):
+        small = Workload(CONFIGS[name].with_batch(P))
+        tr = TiledRows(small, B)
+        st, s0 = tr.step(3), small.step(3)
+        H, K = small.cfg.H, small.cfg.K
+        for key in ("q", "k", "v"):
+            assert np.array_equal(bf16_bits_to_f32(st[key + "_bits"]), st[key]), key
+        for b in rows:
+            s = b // P
+            for h in (0, 5, H - 1):
+                hh = (h + s) % H
+                rot = (s // H) % K
+                for c in (0, 1, 77, K - 1):
+                    assert st["k"][b, h, c] == s0["k"][b % P, hh, (c + rot) % K]
+                assert st["a"][b, h] == np.float32(s0["a"][b % P, hh] * 2.0 ** -((s // H) % 8))
+                e = ((s // H) + s) % 8 - 3
+                assert np.array_equal(st["q"][b, h], (s0["q"][b % P, hh] * 2.0 ** e).astype(np.float32))
+                assert np.array_equal(st["v"][b, h], (s0["v"][b % P, hh] * 2.0 ** e).astype(np.float32))
+                if st["beta"] is not None:
+                    assert st["beta"][b, h] == np.float32(s0["beta"][b % P, hh] * 2.0 ** -((s // H) % 8))
+        for key in ("q", "k", "v", "a"):
+            assert len(np.unique(st[key].reshape(B, -1), axis=0)) == B, (name, key)
