@@ -2,8 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1] [--no-cpu]
 
-K is rounded up to whole periods of the step loop (instances x 16 steps, 64 by
-default) so that every window position and the flush weigh the same.
+K is rounded up to whole periods of the step loop (instances x 16 steps) so
+that every window position and the flush weigh the same.
 
 A step is one decode step of one layer: the read of every (b, h) item at the
 current window position, plus the flush (apply the 16 buffered tokens, emit the
@@ -132,6 +132,14 @@ def workload_name(cfg, ranks) -> str:
             f"{shared}")
 
 
+def default_instances(cfg, ranks) -> int:
+    """Layer instances to rotate over so that a launch cannot find its data in
+    the 256 MB Infinity Cache: the launches between two of one instance read
+    at least 1 GiB (at least 4 instances, as the Nano-shaped layer needs)."""
+    per_launch = np.mean([read_bytes(cfg, ranks, p) for p in range(cfg.W)])
+    return max(4, int(np.ceil((1 << 30) / per_launch)) + 1)
+
+
 def step_bytes(cfg, ranks, dense_all=False) -> float:
     W = cfg.W
     rd = np.mean([read_bytes(cfg, ranks, p, dense_all) for p in range(W)])
@@ -179,14 +187,59 @@ def _cpu_model() -> str:
 
 
 # ---------------------------------------------------------------------------
+# practical ceilings: the library's streaming probe over 1 GiB
+# ---------------------------------------------------------------------------
+STREAM_BYTES = 1 << 30
+# the read kernel writes about one byte for every eight it reads (y and the
+# appended token against the window, token, sketch and map reads: 10.9% of the
+# c1 launch's algorithmic bytes), so its ceiling is the best 8:1 stream
+MIX_READS_PER_WRITE = 8
+
+
+def stream_ceilings(torch, Bnd, timed, dev) -> dict:
+    """Best rate (read + written bytes per second) of the streaming probe for
+    an 8:1 read:write mix, for reads alone and for a 1:1 copy, each the best
+    of a few launch shapes; and torch's device-to-device copy for reference."""
+    src = torch.ones(STREAM_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty(STREAM_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def rate(write_bytes, unroll, blocks, nt):
+        f = lambda: Bnd.sketchssm_stream_probe(src, STREAM_BYTES, dst, write_bytes, unroll, blocks, nt)  # noqa: E731
+        f()
+        us = timed(f, reps=5) * 1000.0
+        return (STREAM_BYTES + write_bytes) / (us * 1e3)
+
+    def best(write_bytes, shapes):
+        return max((rate(write_bytes, u, b, nt), u, b, nt) for u, b in shapes for nt in (False, True))
+
+    mix = best(STREAM_BYTES // MIX_READS_PER_WRITE, [(8, 0), (16, 0), (8, 2048), (16, 2048)])
+    ro = best(0, [(4, 1024), (8, 1024), (8, 2048), (16, 1024), (16, 2048)])
+    cp = best(STREAM_BYTES, [(4, 0), (8, 0), (8, 4096)])
+    half = src[: STREAM_BYTES // 8]      # 512 MB, twice the Infinity Cache
+    other = dst[: STREAM_BYTES // 8]
+    other.copy_(half)
+    tc_us = timed(lambda: other.copy_(half), reps=5) * 1000.0
+    out = {"mix_GBps": round(mix[0], 1),
+           "mix_desc": f"best {MIX_READS_PER_WRITE}:1 read:write stream of 1 GiB read (streaming probe, "
+                       f"unroll {mix[1]}, {'one block per chunk' if mix[2] == 0 else f'{mix[2]} blocks'}, "
+                       f"{'non-temporal' if mix[3] else 'plain'} loads and stores)",
+           "read_only_GBps": round(ro[0], 1), "copy_GBps": round(cp[0], 1),
+           "torch_copy_GBps": round(2 * half.numel() * 4 / (tc_us * 1e3), 1)}
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=256)
     ap.add_argument("--config", default="c1")
-    ap.add_argument("--instances", type=int, default=4,
-                    help="independent layer instances the steps rotate over")
+    ap.add_argument("--instances", type=int, default=0,
+                    help="independent layer instances the steps rotate over (default: enough that the other "
+                         "instances' reads between two launches of one instance cover 1 GiB, at least 4)")
     ap.add_argument("--layers", type=int, default=0,
                     help="model decode loop over N recurrent layers (sets --instances N; e.g. 27 for the Nano model)")
     ap.add_argument("--calibration", default=None,
@@ -231,7 +284,7 @@ def main():
         import dataclasses
         cfg = dataclasses.replace(cfg, kq_heads=args.kq_heads)
     W = cfg.W
-    NI = args.layers or args.instances
+    NI = args.layers or args.instances or default_instances(cfg, Workload(cfg).ranks)
     wl = Workload(cfg)
     cal = None
     if args.calibration:
@@ -255,26 +308,39 @@ def main():
         wli = wl if cal is None else Workload(cfg, ranks=wl.ranks, basis=cal["omega"][i % len(cal["omega"])])
         lays.append(layer_for_workload(wli, device=dev, S_init=lay0.S))
     host_steps = [wl.step(t) for t in range(W)]
-    inputs = [lay0.upload_step(st) for st in host_steps]
+    inputs0 = [lay0.upload_step(st) for st in host_steps]
+
+    def rolled(d, i):
+        # instance i's own copy of a step's inputs: the batch rows rotated by
+        # 37 i, so every launch reads token inputs no other launch has touched
+        return {key: None if x is None else torch.roll(x, shifts=37 * i, dims=0).contiguous()
+                for key, x in d.items()}
+
+    inputs = [inputs0 if i == 0 else [rolled(d, i) for d in inputs0] for i in range(NI)]
     log(f"inputs generated ({time.time() - t0:.1f}s)")
     dense_plan = Bnd.Plan(lay0.shape, np.zeros(cfg.H, np.int32), wl.groups)
     for L in lays:
         L.flush(0)
     torch.cuda.synchronize()
 
+    idx = {id(L): i for i, L in enumerate(lays)}
+
+    def tok(L, pos):
+        return inputs[idx[id(L)]][pos]
+
     def read(L, pos, y=None):
-        d = inputs[pos]
+        d = tok(L, pos)
         return L.read(pos, d["q"], d["k"], d["v"], d["a"], d["beta"], y=y)
 
     def dense_read(L, pos):
-        d = inputs[pos]
+        d = tok(L, pos)
         return L.dense_read(pos, d["q"], d["k"], d["v"], d["a"], d["beta"])
 
     def dense_flush(L, n):
         Bnd.sketchssm_flush(dense_plan, L.S, None, None, L.kbuf, L.vbuf, L.abuf, L.bbuf, n)
 
     def read_flush(L, dense=False):
-        d = inputs[W - 1]
+        d = tok(L, W - 1)
         return L.read_flush(d["q"], d["k"], d["v"], d["a"], d["beta"], plan=dense_plan if dense else None)
 
     def run_steps(n, s0, dense=False, fused=True):
@@ -388,7 +454,7 @@ def main():
             L = lays[i]
             k = (s // NI) % W
             pv, rows, cnt = seq_tabs[k]
-            d = inputs[k]
+            d = inputs[i][k]
             if flush_done[i] is not None:
                 main_stream.wait_event(flush_done[i])
                 flush_done[i] = None
@@ -415,19 +481,14 @@ def main():
 
     # ---- standard per-token decode: every token reads and writes the state ------
     def rmw(L, pos):
-        d = inputs[pos]
+        d = tok(L, pos)
         return L.rmw_step(d["q"], d["k"], d["v"], d["a"], d["beta"])
 
     [rmw(L, 0) for L in lays]
     rmw_us = timed(lambda: [rmw(L, p) for p in range(W) for L in lays], reps=2) * 1000.0 / (NI * W)
 
-    # ---- a device-to-device copy of 1 GiB: the practical read+write HBM rate on this GPU
-    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    copy_us = timed(lambda: dst.copy_(src), reps=5) * 1000.0
-    copy_GBps = 2 * src.numel() * 4 / (copy_us * 1e3)
-    del src, dst
+    # ---- practical HBM ceilings on this GPU, measured in the same run --------
+    ceil = stream_ceilings(torch, Bnd, timed, dev)
 
     ranks = wl.ranks
     rb = [read_bytes(cfg, ranks, p) for p in range(W)]
@@ -458,7 +519,8 @@ def main():
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(cfg.name),
                      "bytes_per_launch": int(rb_avg), "avg_launch_us": round(read_us, 3),
-                     "measured_copy_GBps": round(copy_GBps, 1), "frac_of_measured_copy": round(achieved / copy_GBps, 4)},
+                     "ceiling_GBps": ceil["mix_GBps"], "ceiling": ceil["mix_desc"],
+                     "frac_of_ceiling": round(achieved / ceil["mix_GBps"], 4)},
         "detail": {
             "read_us_mean": round(read_us, 3),
             "read_us_per_pos": [round(x, 2) for x in per_pos],
@@ -482,6 +544,9 @@ def main():
             "model_token_us_all_layers": round(us_step * NI, 2) if args.layers else None,
             "continuous_batching_step_us": round(seq_step_us, 3),
             "continuous_batching_step_us_flush_side_stream": round(seq_side_us, 3),
+            "stream_read_only_GBps": ceil["read_only_GBps"],
+            "stream_copy_GBps": ceil["copy_GBps"],
+            "torch_copy_GBps": ceil["torch_copy_GBps"],
             "rmw_step_us": round(rmw_us, 2),
             "rmw_GBps": round(rmw_bytes(cfg) / (rmw_us * 1e3), 1),
             "ratio_rmw_over_sketch_step": round(rmw_us / us_step, 3),

@@ -19,5 +19,6 @@ from .binding import (  # noqa: F401
     sketchssm_flush,
     sketchssm_flush_seq,
     sketchssm_rmw_step,
+    sketchssm_stream_probe,
     status_string,
 )

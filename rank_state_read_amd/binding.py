@@ -54,6 +54,7 @@ _PROTOS = {
     "sketchssm_flush_seq": (c_i32, [c_vp] * 10 + [c_i32, c_vp]),
     "sketchssm_decode_read_flush": (c_i32, [c_vp] * 16),
     "sketchssm_status_string": (ctypes.c_char_p, [c_i32]),
+    "sketchssm_stream_probe": (c_i32, [c_vp, ctypes.c_size_t, c_vp, ctypes.c_size_t, c_i32, c_i32, c_i32, c_vp]),
 }
 
 
@@ -209,3 +210,12 @@ def sketchssm_decode_read_flush(plan: Plan, S, Z, frames, basis, q, k, v, a, bet
            lib().sketchssm_decode_read_flush(plan.handle, _ptr(S), _ptr(Z), _ptr(frames), _ptr(basis), _ptr(q),
                                              _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(kbuf), _ptr(vbuf),
                                              _ptr(abuf), _ptr(bbuf), _ptr(y), _stream(stream)))
+
+
+def sketchssm_stream_probe(src, read_bytes: int, dst, write_bytes: int, unroll: int = 8, blocks: int = 0,
+                           nontemporal: bool = False, stream=None):
+    """Measurement aid (include/sketchssm_measure.h): stream read_bytes of src,
+    writing write_bytes of sums to dst."""
+    _check("sketchssm_stream_probe",
+           lib().sketchssm_stream_probe(_ptr(src), int(read_bytes), _ptr(dst), int(write_bytes), int(unroll),
+                                        int(blocks), 1 if nontemporal else 0, _stream(stream)))

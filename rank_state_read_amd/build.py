@@ -16,7 +16,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libsketchssm.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-HIP_SOURCES = ["read.hip", "flush.hip", "rmw.hip"]
+HIP_SOURCES = ["read.hip", "flush.hip", "rmw.hip", "stream.hip"]
 CXX_SOURCES = ["plan.cpp"]
 
 # Packed-fp32 VALU forms are kept out of the generated code.

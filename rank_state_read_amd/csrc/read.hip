@@ -92,7 +92,9 @@ __device__ __forceinline__ float raw_dot8(const typename Vec8<QT>::raw_t& a, con
     }
 }
 
-template <int KIND, int V, typename QT, bool DEEP = false>
+// UPOS: the window position is the same for every row of a wave (a lockstep
+// launch, or a dense item's block); a slot's byte offset is then wave-uniform.
+template <int KIND, int V, typename QT, bool DEEP = false, bool UPOS = true>
 struct RowSweep {
     static constexpr bool KDA = KIND == SKSSM_KDA;
     static constexpr bool DELTA = KIND != SKSSM_MAMBA2;
@@ -148,19 +150,23 @@ struct RowSweep {
         const size_t item = size_t(b) * A.H + h;
         const int kh = h / A.share;                  // key/query head
         const size_t itemk = size_t(b) * A.Hk + kh;
-        // window slot i of this item: [W][H][B] layout, slot-major (keys: [W][Hk][B])
-        auto wslot = [&](int i) { return (size_t(i) * A.H + h) * A.B + b; };
-        auto wslotk = [&](int i) { return (size_t(i) * A.Hk + kh) * A.B + b; };
         const bool vl = l < V / 8;
         // lanes >= V/8 own no value elements; they re-read lane 0's chunk (in
         // bounds, never stored) so that no load sits in a divergent branch,
         // which would make the compiler wait for it at the branch's end
         const int vo = vl ? 8 * l : 0;
-        qr = V8::load(A.q, itemk * kK + 8 * l);
-        const typename V8::raw_t kc = V8::load(A.k, itemk * kK + 8 * l);
-        const typename V8::raw_t vc = V8::load(A.v, item * V + vo);
+        // q and k are streamed unless several heads share them (then reused)
+        typename V8::raw_t kc;
+        if (A.share > 1) {
+            qr = V8::load(A.q, itemk * kK + 8 * l);
+            kc = V8::load(A.k, itemk * kK + 8 * l);
+        } else {
+            qr = V8::load_nt(A.q, itemk * kK + 8 * l);
+            kc = V8::load_nt(A.k, itemk * kK + 8 * l);
+        }
+        const typename V8::raw_t vc = V8::load_nt(A.v, item * V + vo);
         float ac[NA];
-        if (KDA) load8f(A.a + item * kK + 8 * l, ac);
+        if (KDA) load8f_nt(A.a + item * kK + 8 * l, ac);
         else ac[0] = A.a[item];
         const float bc = DELTA ? A.beta[item] : 1.f;
         // keep the token's loads together: the staging stores below must not
@@ -196,24 +202,61 @@ struct RowSweep {
             }
         }
 
+        // The window arrays as buffer resources: a slot adds a fixed byte
+        // stride, the item and lane a per-lane byte offset (one register per
+        // array for every slot).  Each array is below 2^31 bytes for every
+        // shape the plan accepts.
+        const uint32_t kstride = uint32_t(A.Hk) * uint32_t(A.B) * (kK * E);
+        const uint32_t vstride = uint32_t(A.H) * uint32_t(A.B) * (V * E);
+        const uint32_t astride = uint32_t(A.H) * uint32_t(A.B) * (NA == 8 ? kK * 4 : 4);
+        const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(A.kbuf, kW * kstride);
+        const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(A.vbuf, kW * vstride);
+        const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(A.abuf, kW * astride);
+        const uint32_t bstride = uint32_t(A.H) * uint32_t(A.B) * 4;
+        const __amdgpu_buffer_rsrc_t brs = buffer_rsrc(A.bbuf, DELTA ? kW * bstride : 0);
+        const uint32_t ko = uint32_t((size_t(kh) * A.B + b) * kK + 8 * l) * E;
+        const uint32_t vo_b = uint32_t((size_t(h) * A.B + b) * V + vo) * E;
+        const uint32_t hb = uint32_t(size_t(h) * A.B + b);
+        const uint32_t ao = KDA ? (hb * kK + 8 * l) * 4 : hb * 4;
         for (int i0 = pos - 1; i0 >= 0; i0 -= CH) {
             typename V8::raw_t kw[CH], vw[CH];
             float aw[CH][NA], bw[CH];
+            // every slot of the chunk is loaded (a slot before the window's
+            // start re-reads slot 0) and the ones past the start are then
+            // masked: the loads stay free of branches
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
-                const int i = i0 - j;
-                kw[j] = V8::zero();
-                vw[j] = V8::zero();
+                const uint32_t ic = uint32_t(i0 - j >= 0 ? i0 - j : 0);
+                // a uniform slot offset goes in the scalar offset, else in the lane's
+                auto off = [&](uint32_t lane, uint32_t stride, uint32_t& v) {
+                    v = UPOS ? lane : lane + ic * stride;
+                    return UPOS ? ic * stride : 0u;
+                };
+                uint32_t vk, vv, va, vb;
+                const uint32_t sk = off(ko, kstride, vk), sv = off(vo_b, vstride, vv);
+                const uint32_t sa = off(ao, astride, va), sb = off(hb * 4, bstride, vb);
+                if (A.share > 1) kw[j] = V8::load_buf(krs, vk, sk);
+                else kw[j] = V8::load_buf_nt(krs, vk, sk);
+                vw[j] = V8::load_buf_nt(vrs, vv, sv);
+                if (KDA) {
+                    const uint4 a0 = buffer_load_u4_nt(ars, va, sa);
+                    const uint4 a1 = buffer_load_u4_nt(ars, va + 16, sa);
+                    const uint32_t aa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-                for (int e = 0; e < NA; ++e) aw[j][e] = 1.f;
-                bw[j] = 0.f;
-                if (i >= 0) {
-                    const size_t si = wslot(i);
-                    kw[j] = V8::load(A.kbuf, wslotk(i) * kK + 8 * l);
-                    if (vl) vw[j] = V8::load(A.vbuf, si * V + 8 * l);
-                    if (KDA) load8f(A.abuf + si * kK + 8 * l, aw[j]);
-                    else aw[j][0] = A.abuf[si];
-                    if (DELTA) bw[j] = A.bbuf[si];
+                    for (int e = 0; e < NA; ++e) aw[j][e] = __uint_as_float(aa[e]);
+                } else {
+                    aw[j][0] = buffer_load_f32(ars, int(va), int(sa));
+                }
+                bw[j] = DELTA ? buffer_load_f32(brs, int(vb), int(sb)) : 0.f;
+            }
+#pragma unroll
+            for (int j = 1; j < CH; ++j) {
+                if (i0 - j < 0) {
+                    kw[j] = V8::zero();
+                    vw[j] = V8::zero();
+#pragma unroll
+                    for (int e = 0; e < NA; ++e) aw[j][e] = 1.f;
+                    bw[j] = 0.f;
                 }
             }
 #pragma unroll
@@ -255,7 +298,7 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
     constexpr int VL = V / 8;
     constexpr bool M2 = KIND == SKSSM_MAMBA2;
     using V8 = Vec8<QT>;
-    using RS = RowSweep<KIND, V, QT, !SEQ>;
+    using RS = RowSweep<KIND, V, QT, !SEQ, !SEQ>;
     // LDS: kRows token staging rows, then the coefficient map
     constexpr int kMapOff4 = kRows * RS::kStageBytes / 16;
     char* stg = reinterpret_cast<char*>(lds4) + (threadIdx.x >> 4) * RS::kStageBytes;
@@ -416,7 +459,7 @@ __device__ __forceinline__ void dense_block(const ReadArgs& A, const HeadTable& 
     for (int j = 0; j < PH; ++j) {
         const int kk = kg + KG * j;
         sreg[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (owner && kk < K) sreg[j] = S4[kk * V4 + v4];
+        if (owner && kk < K) sreg[j] = ldnt_f4(reinterpret_cast<const float*>(S4 + kk * V4 + v4));
     }
     if (tid < 16) {
         using RS = RowSweep<KIND, V, QT, !SEQ>;
@@ -443,7 +486,7 @@ __device__ __forceinline__ void dense_block(const ReadArgs& A, const HeadTable& 
             for (int j = 0; j < PH; ++j) {
                 const int kk = kg + KG * (m0 + j);
                 sreg[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (owner && kk < K) sreg[j] = S4[kk * V4 + v4];
+                if (owner && kk < K) sreg[j] = ldnt_f4(reinterpret_cast<const float*>(S4 + kk * V4 + v4));
             }
         }
 #pragma unroll

@@ -6,6 +6,7 @@
 #include <stdlib.h>
 
 #include "sketchssm.h"
+#include "sketchssm_measure.h"
 
 static void print_row(const char* name, const int32_t* x, int n) {
     int i;
@@ -54,6 +55,7 @@ int main(void) {
     sh.V = 80;
     printf("flush_null_plan %d\n", (int)sketchssm_flush(NULL, NULL, NULL, NULL, NULL, NULL, NULL,
                                                         NULL, 0, NULL));
+    printf("probe_null %d\n", (int)sketchssm_stream_probe(NULL, 4096 * 8, NULL, 0, 8, 1, 0, NULL));
     printf("status_text %s\n", sketchssm_status_string(SKSSM_EALIGN));
     return 0;
 }

@@ -15,10 +15,16 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared_symbols():
-    with open(os.path.join(ROOT, "include", "sketchssm.h")) as f:
-        text = f.read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sketchssm_[a-z_]+)\s*\(", text)))
+    syms = set()
+    inc = os.path.join(ROOT, "include")
+    for name in sorted(os.listdir(inc)):
+        if not name.endswith(".h"):
+            continue
+        with open(os.path.join(inc, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        syms |= set(re.findall(r"\b(sketchssm_[a-z_]+)\s*\(", text))
+    return sorted(syms)
 
 
 def test_library_exports_every_declared_symbol():
@@ -225,3 +231,19 @@ def test_status_strings():
     for s in range(7):
         assert B.status_string(s)
     assert "unknown" in B.status_string(42)
+
+
+def test_stream_probe_argument_errors():
+    """The measurement probe's argument rules are checked before any launch."""
+    L = B.lib()
+    a16 = 1 << 20            # a 16-byte-aligned stand-in address (never dereferenced)
+    probe = L.sketchssm_stream_probe
+    assert probe(None, 8 * 4096, a16, 0, 8, 4, 0, None) == 1            # null source
+    assert probe(a16 + 4, 8 * 4096, a16, 0, 8, 4, 0, None) == 3         # unaligned
+    assert probe(a16, 8 * 4096, a16, 0, 6, 4, 0, None) == 1             # unroll not 4/8/16
+    assert probe(a16, 8 * 4096 + 16, a16, 0, 8, 4, 0, None) == 2        # not whole chunks
+    assert probe(a16, 8 * 4096, a16, 3 * 4096, 8, 0, 0, None) == 2      # ratio not an integer
+    assert probe(a16, 16 * 4096, a16, 4096, 8, 0, 0, None) == 2         # ratio 16 > unroll 8
+    assert probe(a16, 8 * 4096, a16, 0, 8, 0, 0, None) == 1             # read-only needs a bounded grid
+    assert probe(a16, 8 * 4096, a16, 0, 8, -1, 0, None) == 1            # negative grid
+    assert probe(a16, 8 * 4096, a16, 0, 8, 4, 2, None) == 1             # unknown flag

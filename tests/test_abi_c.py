@@ -1,5 +1,5 @@
 """The ABI from plain C: tests/abi_client.c is compiled as C99 with warnings as
-errors against include/sketchssm.h, linked to the built library and run on the
+errors against include/sketchssm.h and include/sketchssm_measure.h, linked to the built library and run on the
 host (planner and status codes only, no GPU needed)."""
 import json
 import os
@@ -42,4 +42,5 @@ def test_c_client(tmp_path, golden_dir):
     assert int(out["null_out"]) == 1      # SKSSM_EINVAL
     assert int(out["bad_V"]) == 2         # SKSSM_ESHAPE
     assert int(out["flush_null_plan"]) == 1
+    assert int(out["probe_null"]) == 1    # SKSSM_EINVAL
     assert "aligned" in out["status_text"]
