@@ -233,9 +233,7 @@ sketchssm_status sketchssm_flush_seq(const sketchssm_plan* plan, float* S, float
  * to the Full State, Read from a Compact Sketch": buffered keys and values,
  * reads from the stored sketch; dense heads output S_n^T q).  The window's
  * slots 0 .. W-2 are read; the current token is taken from q, k, v, a, beta
- * (the window restarts at slot 0 afterwards).  One pass for Mamba-2 and KDA;
- * for GDN, where the fused pass measured slower, the same call runs the read
- * and then the flush.
+ * (the window restarts at slot 0 afterwards).  One pass for every layer kind.
  *   S, Z          as in sketchssm_flush (Z is read as the old sketch, then
  *                 overwritten with the new one)
  *   frames        as in sketchssm_decode_read; basis as in sketchssm_flush

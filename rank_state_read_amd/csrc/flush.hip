@@ -128,11 +128,11 @@ __device__ __forceinline__ float pick(const float (&x)[N], int i) {
 constexpr int kFlushWavesPerEu = 6;
 
 // FUSED: the read of the window's last token and the flush of the full window
-// in one pass (see sketchssm_decode_read_flush; Mamba-2 and KDA); the KDA
-// instances then take a 96-VGPR budget.
+// in one pass (see sketchssm_decode_read_flush); the fused KDA instances take
+// a 96-VGPR budget, the others fit the plain flush's 80.
 template <int KIND, int V, typename QT, bool FUSED>
 __global__ __launch_bounds__(V / 16 * 64)
-__attribute__((amdgpu_waves_per_eu((FUSED && KIND != SKSSM_MAMBA2) ? 5 : kFlushWavesPerEu)))
+__attribute__((amdgpu_waves_per_eu((FUSED && KIND == SKSSM_KDA) ? 5 : kFlushWavesPerEu)))
 void flush_kernel(FlushArgs A, HeadTable T) {
     using V8 = Vec8<QT>;
     using L = FlushLds<KIND, V, FUSED>;
@@ -703,11 +703,7 @@ template <int KIND, int V, typename QT>
 static hipError_t launch_flush_t(const FlushArgs& a, const HeadTable& t, int grid,
                                  hipStream_t s) {
     if (!a.y) return launch_flush_f<KIND, V, QT, false>(a, t, grid, s);
-    if constexpr (KIND == SKSSM_GDN) {
-        return hipErrorInvalidValue;  // GDN runs the last read and the flush apart
-    } else {
-        return launch_flush_f<KIND, V, QT, true>(a, t, grid, s);
-    }
+    return launch_flush_f<KIND, V, QT, true>(a, t, grid, s);
 }
 
 template <int KIND, typename QT>
@@ -841,16 +837,6 @@ extern "C" sketchssm_status sketchssm_decode_read_flush(const sketchssm_plan* pl
                                                        void* vbuf, float* abuf, float* bbuf, float* y,
                                                        void* stream) {
     if (!plan) return SKSSM_EINVAL;
-    if (plan->shape.kind == SKSSM_GDN) {
-        // For GDN the fused pass needs a 96-VGPR budget, which costs the flush a
-        // third of its resident blocks and more than the separate last read
-        // (measured 302 against 256 + 23 us at 256 x 32 heads): read, then flush.
-        const sketchssm_status st = sketchssm_decode_read(plan, S, Z, frames, q, k, v, a, beta, kbuf,
-                                                          vbuf, abuf, bbuf, plan->shape.W - 1, y,
-                                                          stream);
-        if (st != SKSSM_OK) return st;
-        return sketchssm_flush(plan, S, Z, basis, kbuf, vbuf, abuf, bbuf, plan->shape.W, stream);
-    }
     const FusedRead fr{frames, q, k, v, a, beta, y};
     return run_flush(plan, S, Z, basis, kbuf, vbuf, abuf, bbuf, plan->shape.W, nullptr, nullptr, 0,
                      stream, &fr);
