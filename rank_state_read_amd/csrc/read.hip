@@ -155,6 +155,58 @@ struct RowSweep {
         // bounds, never stored) so that no load sits in a divergent branch,
         // which would make the compiler wait for it at the branch's end
         const int vo = vl ? 8 * l : 0;
+        // The window arrays as buffer resources: a slot adds a fixed byte
+        // stride, the item and lane a per-lane byte offset (one register per
+        // array for every slot).  Each array is below 2^31 bytes for every
+        // shape the plan accepts.
+        const uint32_t kstride = uint32_t(A.Hk) * uint32_t(A.B) * (kK * E);
+        const uint32_t vstride = uint32_t(A.H) * uint32_t(A.B) * (V * E);
+        const uint32_t astride = uint32_t(A.H) * uint32_t(A.B) * (NA == 8 ? kK * 4 : 4);
+        const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(A.kbuf, kW * kstride);
+        const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(A.vbuf, kW * vstride);
+        const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(A.abuf, kW * astride);
+        const uint32_t bstride = uint32_t(A.H) * uint32_t(A.B) * 4;
+        const __amdgpu_buffer_rsrc_t brs = buffer_rsrc(A.bbuf, DELTA ? kW * bstride : 0);
+        const uint32_t ko = uint32_t((size_t(kh) * A.B + b) * kK + 8 * l) * E;
+        const uint32_t vo_b = uint32_t((size_t(h) * A.B + b) * V + vo) * E;
+        const uint32_t hb = uint32_t(size_t(h) * A.B + b);
+        const uint32_t ao = KDA ? (hb * kK + 8 * l) * 4 : hb * 4;
+        typename V8::raw_t kw[CH], vw[CH];
+        float aw[CH][NA], bw[CH];
+        // every slot of a chunk is loaded (a slot before the window's start
+        // re-reads slot 0) and the ones past the start are then masked: the
+        // loads stay free of branches
+        auto load_chunk = [&](int i0) {
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const uint32_t ic = uint32_t(i0 - j >= 0 ? i0 - j : 0);
+                // a uniform slot offset goes in the scalar offset (read from
+                // the first lane, so that it stays in a scalar register even
+                // where the compiler computes it with a vector instruction),
+                // else in the lane's
+                auto off = [&](uint32_t lane, uint32_t stride, uint32_t& v) {
+                    v = UPOS ? lane : lane + ic * stride;
+                    return UPOS ? uint32_t(__builtin_amdgcn_readfirstlane(int(ic * stride))) : 0u;
+                };
+                uint32_t vk, vv, va, vb;
+                const uint32_t sk = off(ko, kstride, vk), sv = off(vo_b, vstride, vv);
+                const uint32_t sa = off(ao, astride, va), sb = off(hb * 4, bstride, vb);
+                if (A.share > 1) kw[j] = V8::load_buf(krs, vk, sk);
+                else kw[j] = V8::load_buf_nt(krs, vk, sk);
+                vw[j] = V8::load_buf_nt(vrs, vv, sv);
+                if (KDA) {
+                    const uint4 a0 = buffer_load_u4_nt(ars, va, sa);
+                    const uint4 a1 = buffer_load_u4_nt(ars, va + 16, sa);
+                    const uint32_t aa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+                    for (int e = 0; e < NA; ++e) aw[j][e] = __uint_as_float(aa[e]);
+                } else {
+                    aw[j][0] = buffer_load_f32(ars, int(va), int(sa));
+                }
+                bw[j] = DELTA ? buffer_load_f32(brs, int(vb), int(sb)) : 0.f;
+            }
+        };
+
         // q and k are streamed unless several heads share them (then reused)
         typename V8::raw_t kc;
         if (A.share > 1) {
@@ -202,53 +254,8 @@ struct RowSweep {
             }
         }
 
-        // The window arrays as buffer resources: a slot adds a fixed byte
-        // stride, the item and lane a per-lane byte offset (one register per
-        // array for every slot).  Each array is below 2^31 bytes for every
-        // shape the plan accepts.
-        const uint32_t kstride = uint32_t(A.Hk) * uint32_t(A.B) * (kK * E);
-        const uint32_t vstride = uint32_t(A.H) * uint32_t(A.B) * (V * E);
-        const uint32_t astride = uint32_t(A.H) * uint32_t(A.B) * (NA == 8 ? kK * 4 : 4);
-        const __amdgpu_buffer_rsrc_t krs = buffer_rsrc(A.kbuf, kW * kstride);
-        const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(A.vbuf, kW * vstride);
-        const __amdgpu_buffer_rsrc_t ars = buffer_rsrc(A.abuf, kW * astride);
-        const uint32_t bstride = uint32_t(A.H) * uint32_t(A.B) * 4;
-        const __amdgpu_buffer_rsrc_t brs = buffer_rsrc(A.bbuf, DELTA ? kW * bstride : 0);
-        const uint32_t ko = uint32_t((size_t(kh) * A.B + b) * kK + 8 * l) * E;
-        const uint32_t vo_b = uint32_t((size_t(h) * A.B + b) * V + vo) * E;
-        const uint32_t hb = uint32_t(size_t(h) * A.B + b);
-        const uint32_t ao = KDA ? (hb * kK + 8 * l) * 4 : hb * 4;
         for (int i0 = pos - 1; i0 >= 0; i0 -= CH) {
-            typename V8::raw_t kw[CH], vw[CH];
-            float aw[CH][NA], bw[CH];
-            // every slot of the chunk is loaded (a slot before the window's
-            // start re-reads slot 0) and the ones past the start are then
-            // masked: the loads stay free of branches
-#pragma unroll
-            for (int j = 0; j < CH; ++j) {
-                const uint32_t ic = uint32_t(i0 - j >= 0 ? i0 - j : 0);
-                // a uniform slot offset goes in the scalar offset, else in the lane's
-                auto off = [&](uint32_t lane, uint32_t stride, uint32_t& v) {
-                    v = UPOS ? lane : lane + ic * stride;
-                    return UPOS ? ic * stride : 0u;
-                };
-                uint32_t vk, vv, va, vb;
-                const uint32_t sk = off(ko, kstride, vk), sv = off(vo_b, vstride, vv);
-                const uint32_t sa = off(ao, astride, va), sb = off(hb * 4, bstride, vb);
-                if (A.share > 1) kw[j] = V8::load_buf(krs, vk, sk);
-                else kw[j] = V8::load_buf_nt(krs, vk, sk);
-                vw[j] = V8::load_buf_nt(vrs, vv, sv);
-                if (KDA) {
-                    const uint4 a0 = buffer_load_u4_nt(ars, va, sa);
-                    const uint4 a1 = buffer_load_u4_nt(ars, va + 16, sa);
-                    const uint32_t aa[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-                    for (int e = 0; e < NA; ++e) aw[j][e] = __uint_as_float(aa[e]);
-                } else {
-                    aw[j][0] = buffer_load_f32(ars, int(va), int(sa));
-                }
-                bw[j] = DELTA ? buffer_load_f32(brs, int(vb), int(sb)) : 0.f;
-            }
+            load_chunk(i0);
 #pragma unroll
             for (int j = 1; j < CH; ++j) {
                 if (i0 - j < 0) {
@@ -346,6 +353,22 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
     };
     stage_map(0);
 
+    // y = sum_m (F_m . q~) Z_m + intra, ZR sketch rows per round trip (four
+    // for the lockstep bf16 GDN instances, which have the registers, else two)
+    constexpr int ZR = (!SEQ && KIND == SKSSM_GDN && std::is_same<QT, Bf16Tag>::value) ? 4 : 2;
+    float z[ZR][8];
+    auto load_z = [&](int m, int mend) {
+#pragma unroll
+        for (int j = 0; j < ZR; ++j)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) z[j][e] = 0.f;
+        if (l < VL) {
+#pragma unroll
+            for (int j = 0; j < ZR; ++j)
+                if (m + j < mend) load8f(Zi + size_t(m + j) * V + 8 * l, z[j]);
+        }
+    };
+
     typename V8::raw_t qr;
     float u[8], acc[8], gtot = 1.f;
     if (SEQ) {
@@ -368,9 +391,6 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
         for (int e = 0; e < 8; ++e) u[e] = gtot * q[e];
     }
 
-    // y = sum_m (F_m . q~) Z_m + intra, ZR sketch rows per round trip (four
-    // for the lockstep bf16 GDN instances, which have the registers, else two)
-    constexpr int ZR = (!SEQ && KIND == SKSSM_GDN && std::is_same<QT, Bf16Tag>::value) ? 4 : 2;
     for (int m0 = 0; m0 < r; m0 += kMapRows) {
         if (m0 > 0) {
             __syncthreads();  // every row is done with the previous piece
@@ -381,16 +401,7 @@ __device__ __forceinline__ void sketch_block(const ReadArgs& A, const HeadTable&
         const int mend = min(r, m0 + kMapRows);
         if (!active) continue;
         for (int m = m0; m < mend; m += ZR) {
-            float z[ZR][8];
-#pragma unroll
-            for (int j = 0; j < ZR; ++j)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) z[j][e] = 0.f;
-            if (l < VL) {
-#pragma unroll
-                for (int j = 0; j < ZR; ++j)
-                    if (m + j < mend) load8f(Zi + size_t(m + j) * V + 8 * l, z[j]);
-            }
+            load_z(m, mend);
 #pragma unroll
             for (int j = 0; j < ZR; ++j) {
                 if (m + j < mend) {
