@@ -199,14 +199,29 @@ MIX_READS_PER_WRITE = 8
 def stream_ceilings(torch, Bnd, timed, dev) -> dict:
     """Best rate (read + written bytes per second) of the streaming probe for
     an 8:1 read:write mix, for reads alone and for a 1:1 copy, each the best
-    of a few launch shapes; and torch's device-to-device copy for reference."""
-    src = torch.ones(STREAM_BYTES // 4, dtype=torch.float32, device=dev)
-    dst = torch.empty(STREAM_BYTES // 4, dtype=torch.float32, device=dev)
+    of a few launch shapes; and torch's device-to-device copy for reference.
+
+    Like the decode kernels, which rotate over layer instances, the probe
+    never finds its data in the 256 MB last-level cache: successive launches
+    read the two 1 GiB sources in turn and write successive parts of a 2 GiB
+    destination pool (the 128 MB written by one 8:1 launch would otherwise
+    stay in that cache from one launch to the next)."""
+    srcs = [torch.ones(STREAM_BYTES // 4, dtype=torch.float32, device=dev) for _ in range(2)]
+    pool = torch.empty(2 * STREAM_BYTES // 4, dtype=torch.float32, device=dev)
+    turn = [0]
+
+    def launch(write_bytes, unroll, blocks, nt):
+        i = turn[0]
+        turn[0] += 1
+        span = max(write_bytes, 4096 * max(blocks, 1))  # bytes this launch writes
+        slot = i % max(1, pool.numel() * 4 // span)
+        dst = pool[slot * span // 4:]
+        Bnd.sketchssm_stream_probe(srcs[i % 2], STREAM_BYTES, dst, write_bytes, unroll, blocks, nt)
 
     def rate(write_bytes, unroll, blocks, nt):
-        f = lambda: Bnd.sketchssm_stream_probe(src, STREAM_BYTES, dst, write_bytes, unroll, blocks, nt)  # noqa: E731
+        f = lambda: launch(write_bytes, unroll, blocks, nt)  # noqa: E731
         f()
-        us = timed(f, reps=5) * 1000.0
+        us = timed(f, reps=6) * 1000.0
         return (STREAM_BYTES + write_bytes) / (us * 1e3)
 
     def best(write_bytes, shapes):
@@ -215,17 +230,17 @@ def stream_ceilings(torch, Bnd, timed, dev) -> dict:
     mix = best(STREAM_BYTES // MIX_READS_PER_WRITE, [(8, 0), (16, 0), (8, 2048), (16, 2048)])
     ro = best(0, [(4, 1024), (8, 1024), (8, 2048), (16, 1024), (16, 2048)])
     cp = best(STREAM_BYTES, [(4, 0), (8, 0), (8, 4096)])
-    half = src[: STREAM_BYTES // 8]      # 512 MB, twice the Infinity Cache
-    other = dst[: STREAM_BYTES // 8]
+    half = srcs[0][: STREAM_BYTES // 8]      # 512 MB, twice the Infinity Cache
+    other = pool[: STREAM_BYTES // 8]
     other.copy_(half)
     tc_us = timed(lambda: other.copy_(half), reps=5) * 1000.0
     out = {"mix_GBps": round(mix[0], 1),
-           "mix_desc": f"best {MIX_READS_PER_WRITE}:1 read:write stream of 1 GiB read (streaming probe, "
+           "mix_desc": f"best {MIX_READS_PER_WRITE}:1 read:write stream of 1 GiB read, rotating buffers (streaming probe, "
                        f"unroll {mix[1]}, {'one block per chunk' if mix[2] == 0 else f'{mix[2]} blocks'}, "
                        f"{'non-temporal' if mix[3] else 'plain'} loads and stores)",
            "read_only_GBps": round(ro[0], 1), "copy_GBps": round(cp[0], 1),
            "torch_copy_GBps": round(2 * half.numel() * 4 / (tc_us * 1e3), 1)}
-    del src, dst
+    del srcs, pool, half, other
     torch.cuda.empty_cache()
     return out
 

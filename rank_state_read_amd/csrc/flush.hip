@@ -655,8 +655,8 @@ void flush_kernel(FlushArgs A, HeadTable T) {
                 const int rows = min(16, r - 16 * mt);
                 const int row = tid / (V / 4), c4 = tid - row * (V / 4);  // 4 V threads: one piece each
                 if (row < rows)
-                    *reinterpret_cast<float4*>(Zi + size_t(16 * mt + row) * V + 4 * c4) =
-                        *reinterpret_cast<const float4*>(sm + row * VS + 4 * c4);
+                    __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(sm + row * VS + 4 * c4),
+                                                reinterpret_cast<f32x4*>(Zi + size_t(16 * mt + row) * V + 4 * c4));
             }
         }
     };
@@ -671,9 +671,11 @@ void flush_kernel(FlushArgs A, HeadTable T) {
                 for (int rr = 0; rr < 4; ++rr) buffer_store_f32(s[kt][rr], srs, svo, (16 * kt + rr) * V * 4);
         } else {
             // whole rows through the window-phase LDS (keys and values), dead
-            // once every wave has applied the update
+            // once every wave has applied the update; streaming stores, as for
+            // the sketch rows (a little faster: neither is read again before
+            // the next flush)
             static_assert(2 * 16 * VS <= L::om, "state tiles overlap the basis tile");
-            store_state_tiles<V>(s, sm, srs, tid);
+            store_state_tiles<V, 16, 2, true>(s, sm, srs, tid);
         }
     } else if (sketch) {
         __syncthreads();

@@ -8,9 +8,11 @@
 
 namespace skssm {
 
+// 16-byte buffer store; NT: non-temporal (streaming) store
+template <bool NT = false>
 __device__ __forceinline__ void buffer_store_f32x4(f32x4 x, __amdgpu_buffer_rsrc_t r, int voff, int soff) {
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, voff, soff, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), r, voff, soff, NT ? 2 : 0);
 }
 
 // Store the K x V state held by V / 16 waves (wave w, lane l, tile kt,
@@ -23,7 +25,8 @@ __device__ __forceinline__ void buffer_store_f32x4(f32x4 x, __amdgpu_buffer_rsrc
 // alternates two staging areas (one barrier per round), NBUF = 1 reuses one
 // (two).  `st` is NBUF x TR x (V + 4) floats of LDS that no wave reads any
 // more; the call begins with a barrier, after which they are overwritten.
-template <int V, int TR = 16, int NBUF = 2>
+// NT: the rows leave as non-temporal stores (nothing reads them back soon).
+template <int V, int TR = 16, int NBUF = 2, bool NT = false>
 __device__ __forceinline__ void store_state_tiles(const f32x4 (&s)[8], float* st, __amdgpu_buffer_rsrc_t srs,
                                                   int tid) {
     static_assert(TR % 16 == 0 && kK % TR == 0 && (NBUF == 1 || NBUF == 2), "tile rows");
@@ -47,7 +50,7 @@ __device__ __forceinline__ void store_state_tiles(const f32x4 (&s)[8], float* st
 #pragma unroll
         for (int j = 0; j < TT; ++j) {
             const f32x4 v = *reinterpret_cast<const f32x4*>(t + (16 * j + row) * VS + 4 * c4);
-            buffer_store_f32x4(v, srs, (row * V + 4 * c4) * 4, (TR * rd + 16 * j) * V * 4);
+            buffer_store_f32x4<NT>(v, srs, (row * V + 4 * c4) * 4, (TR * rd + 16 * j) * V * 4);
         }
     }
 }
