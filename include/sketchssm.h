@@ -36,7 +36,8 @@
  *   - arguments are checked on the host before anything is launched and a
  *     status is returned; nothing throws across this boundary;
  *   - all arrays are dense row-major with the layouts written beside them.
- * Supported shapes: K = 128, W = 16, V in {64, 80, 128}, 1 <= H <= 256,
+ * Supported shapes: K = 128, W = 16, V a multiple of 16 from 64 to 128 (the
+ * Nano layer's 80, GDN/KDA's 128), 1 <= H <= 256,
  * rank_cap <= 64.  Below, Hk = kq_heads (or H when 0) and head h uses key/query
  * head h / (H / Hk).
  */
@@ -77,7 +78,7 @@ typedef struct {
     int32_t B;          /* batch (sequences) */
     int32_t H;          /* state heads of the layer */
     int32_t K;          /* key dim (128) */
-    int32_t V;          /* value dim (64, 80 or 128) */
+    int32_t V;          /* value dim: 64, 80, 96, 112 or 128 */
     int32_t W;          /* window length between flushes (16) */
     int32_t G;          /* basis groups */
     int32_t basis_rows; /* rows per group basis (79 on the Nano card) */

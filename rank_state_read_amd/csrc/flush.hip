@@ -714,6 +714,8 @@ static hipError_t launch_flush_v(int V, const FlushArgs& a, const HeadTable& t, 
     switch (V) {
         case 64: return launch_flush_t<KIND, 64, QT>(a, t, grid, s);
         case 80: return launch_flush_t<KIND, 80, QT>(a, t, grid, s);
+        case 96: return launch_flush_t<KIND, 96, QT>(a, t, grid, s);
+        case 112: return launch_flush_t<KIND, 112, QT>(a, t, grid, s);
         case 128: return launch_flush_t<KIND, 128, QT>(a, t, grid, s);
     }
     return hipErrorInvalidValue;

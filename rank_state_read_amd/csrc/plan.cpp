@@ -27,7 +27,7 @@ sketchssm_status check_shape(const sketchssm_shape* s) {
     if (s->qkv != SKSSM_BF16 && s->qkv != SKSSM_F32) return SKSSM_EINVAL;
     if (s->B < 1 || s->H < 1 || s->H > kMaxHeads) return SKSSM_ESHAPE;
     if (s->K != kK || s->W != kW) return SKSSM_ESHAPE;
-    if (s->V != 64 && s->V != 80 && s->V != 128) return SKSSM_ESHAPE;
+    if (s->V < 64 || s->V > 128 || s->V % 16 != 0) return SKSSM_ESHAPE;
     if (s->G < 1 || s->G > kMaxHeads) return SKSSM_ESHAPE;
     if (s->basis_rows < 1 || s->rank_cap < 1 || s->rank_cap > kMaxRank) return SKSSM_ESHAPE;
     if (s->kq_heads < 0 || s->kq_heads > s->H || (s->kq_heads > 0 && s->H % s->kq_heads != 0))

@@ -574,6 +574,8 @@ static hipError_t launch_read_v(int V, const ReadArgs& a, const HeadTable& t, in
     switch (V) {
         case 64: return launch_read_t<KIND, 64, QT>(a, t, grid, lds, s);
         case 80: return launch_read_t<KIND, 80, QT>(a, t, grid, lds, s);
+        case 96: return launch_read_t<KIND, 96, QT>(a, t, grid, lds, s);
+        case 112: return launch_read_t<KIND, 112, QT>(a, t, grid, lds, s);
         case 128: return launch_read_t<KIND, 128, QT>(a, t, grid, lds, s);
     }
     return hipErrorInvalidValue;
@@ -642,7 +644,14 @@ static sketchssm_status run_read(const sketchssm_shape& sh, const HeadTable& t, 
     const int map_rows = ((max_rank < kMapRows ? max_rank : kMapRows) + 1) & ~1;
     if (n_sketch > 0) lds = kRows * stage + size_t(map_rows) * kK * sizeof(float);
     if (n_dense > 0) {
-        const size_t dl = (sh.V == 64 ? DenseLds<64>::bytes : sh.V == 80 ? DenseLds<80>::bytes : DenseLds<128>::bytes) + stage;
+        size_t dl = stage;
+        switch (sh.V) {
+            case 64: dl += DenseLds<64>::bytes; break;
+            case 80: dl += DenseLds<80>::bytes; break;
+            case 96: dl += DenseLds<96>::bytes; break;
+            case 112: dl += DenseLds<112>::bytes; break;
+            default: dl += DenseLds<128>::bytes; break;
+        }
         lds = lds > dl ? lds : dl;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -145,6 +145,8 @@ static hipError_t launch_rmw_v(int V, const RmwArgs& a, int grid, hipStream_t s)
     switch (V) {
         case 64: return launch_rmw_t<KIND, 64, QT>(a, grid, s);
         case 80: return launch_rmw_t<KIND, 80, QT>(a, grid, s);
+        case 96: return launch_rmw_t<KIND, 96, QT>(a, grid, s);
+        case 112: return launch_rmw_t<KIND, 112, QT>(a, grid, s);
         case 128: return launch_rmw_t<KIND, 128, QT>(a, grid, s);
     }
     return hipErrorInvalidValue;

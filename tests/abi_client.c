@@ -50,7 +50,7 @@ int main(void) {
     /* status codes, checked on the host before anything could be launched */
     plan = NULL;
     printf("null_out %d\n", (int)sketchssm_plan_create(&sh, rank, group, NULL));
-    sh.V = 96;
+    sh.V = 72;
     printf("bad_V %d\n", (int)sketchssm_plan_create(&sh, rank, group, &plan));
     sh.V = 80;
     printf("flush_null_plan %d\n", (int)sketchssm_flush(NULL, NULL, NULL, NULL, NULL, NULL, NULL,

@@ -73,7 +73,7 @@ def test_plan_hand_example_from_library(golden_dir):
 
 
 @pytest.mark.parametrize("bad", [
-    dict(H=0), dict(H=257), dict(V=96), dict(G=0), dict(cap=65), dict(B_=0),
+    dict(H=0), dict(H=257), dict(V=72), dict(V=48), dict(V=144), dict(G=0), dict(cap=65), dict(B_=0),
     dict(kq=3), dict(kq=16), dict(kq=-1),
     # one layer's state must stay below 2^31 elements: 1639 x 128 x 128 x 80 is past it
     dict(B_=1639, H=128, G=8),
@@ -159,7 +159,7 @@ def test_flush_argument_errors():
 
 def test_dense_read_argument_errors():
     L = B.lib()
-    bad = _shape(V=96)
+    bad = _shape(V=72)
     assert L.sketchssm_dense_read(ctypes.byref(bad), *([FAKE] * 5), None, FAKE, FAKE, FAKE, None, 0,
                                   FAKE, None) == 2
     ok = _shape()
@@ -171,7 +171,7 @@ def test_rmw_step_argument_errors():
     L = B.lib()
     ok = _shape()
     args = [FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE]            # S q k v a beta y
-    assert L.sketchssm_rmw_step(ctypes.byref(_shape(V=96)), *args, None) == 2
+    assert L.sketchssm_rmw_step(ctypes.byref(_shape(V=72)), *args, None) == 2
     assert L.sketchssm_rmw_step(ctypes.byref(ok), *([None] + args[1:]), None) == 1
     assert L.sketchssm_rmw_step(ctypes.byref(ok), *(args[:5] + [FAKE, FAKE]), None) == 1  # beta with Mamba-2
     gdn = _shape(kind="gdn", V=128)

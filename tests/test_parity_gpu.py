@@ -108,7 +108,9 @@ def _edge_cfg(kind, V, B=19, cap=49, qkv="bf16"):
 
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("kind,V", [("mamba2", 80), ("mamba2", 64), ("mamba2", 128), ("gdn", 128),
-                                    ("gdn", 80), ("gdn", 64), ("kda", 128), ("kda", 80), ("kda", 64)])
+                                    ("gdn", 80), ("gdn", 64), ("kda", 128), ("kda", 80), ("kda", 64),
+                                    ("mamba2", 96), ("mamba2", 112), ("gdn", 96), ("gdn", 112),
+                                    ("kda", 96), ("kda", 112)])
 def test_rank_extremes(kind, V):
     """Ranks at 1, at tile edges (16, 17, 32, 33), at the cap, mixed with dense heads."""
     cfg = _edge_cfg(kind, V, cap=64)
@@ -320,7 +322,8 @@ def test_fused_last_read(name, B):
 
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("kind,V,qkv", [("mamba2", 80, "bf16"), ("gdn", 128, "bf16"), ("kda", 128, "bf16"),
-                                        ("mamba2", 64, "f32"), ("gdn", 80, "f32"), ("kda", 64, "f32")])
+                                        ("mamba2", 64, "f32"), ("gdn", 80, "f32"), ("kda", 64, "f32"),
+                                        ("mamba2", 96, "bf16"), ("gdn", 112, "bf16"), ("kda", 96, "f32")])
 def test_fused_last_read_rank_extremes(kind, V, qkv):
     """Map tiles beyond the first (ranks 17 .. 64) and dense heads in the fused read."""
     cfg = _edge_cfg(kind, V, cap=64, qkv=qkv)

@@ -93,7 +93,8 @@ def test_rmw_full_size_sampled(name):
 
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("kind,V,qkv", [("mamba2", 64, "bf16"), ("gdn", 64, "bf16"), ("kda", 80, "bf16"),
-                                        ("mamba2", 128, "f32"), ("gdn", 80, "f32"), ("kda", 128, "f32")])
+                                        ("mamba2", 128, "f32"), ("gdn", 80, "f32"), ("kda", 128, "f32"),
+                                        ("mamba2", 112, "bf16"), ("gdn", 96, "bf16"), ("kda", 112, "f32")])
 def test_rmw_widths_and_dtypes(kind, V, qkv):
     from workloads import Config
     cfg = Config(f"rmw-{kind}-{V}-{qkv}", kind, B=19, H=8, K=128, V=V, G=2, W=16, steps=20, qkv=qkv,

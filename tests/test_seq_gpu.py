@@ -49,10 +49,12 @@ def _schedule(B, T, W, seed):
     return join, idle, early
 
 
-def _run(name, B, T, kq=None):
+def _run(name, B, T, kq=None, V=None):
     import dataclasses
     from rank_state_read_amd.layer import layer_for_workload
     cfg = dataclasses.replace(CONFIGS[name].with_batch(B), kq_heads=kq)
+    if V is not None:
+        cfg = dataclasses.replace(cfg, V=V)
     wl = Workload(cfg)
     W, H = cfg.W, cfg.H
     lay = layer_for_workload(wl)
@@ -133,3 +135,10 @@ def _run(name, B, T, kq=None):
                                        ("c0", 2, None)])
 def test_staggered_windows(name, B, kq):
     _run(name, B, 2 * CONFIGS[name].W + 9, kq)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,V", [("c1", 96), ("c3", 112), ("c4", 96)])
+def test_staggered_windows_other_value_widths(name, V):
+    """Value widths between the headline layers' (every multiple of 16 from 64 to 128 is accepted)."""
+    _run(name, 19, 2 * CONFIGS[name].W + 9, V=V)
