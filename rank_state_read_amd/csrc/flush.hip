@@ -85,7 +85,7 @@ struct FlushLds {
     static constexpr int gw = ap + (delta ? 16 * KS : 0);  // KDA: gamma_W per channel [K]
     static constexpr int vw = gw + (kda ? kK : 0);         // window values [16][VS]
     static constexpr int kg = vw + 16 * VS;                // delta: gamma-scaled keys [16][KS]
-    static constexpr int lt = kg + (delta ? 16 * KS : 0);  // delta: L transposed [16][16]
+    static constexpr int lt = kg + (delta ? 16 * KS : 0);  // delta: L [16][16] (row-major)
     static constexpr int tm = lt + (delta ? 256 : 0);      // delta: T [16][16]
     static constexpr int al = tm + (delta ? 256 : 0);      // KDA: decays [16][K]
     static constexpr int om = al + (kda ? 16 * kK : 0);    // one tile of basis rows [16][K], swizzled
@@ -123,6 +123,30 @@ __device__ __forceinline__ float pick(const float (&x)[N], int i) {
     return r;
 }
 
+// One column of the unit lower-triangular solve (I + L) x = b held by a DPP
+// row, lane i holding x_i and its row of L: step M broadcasts x_M (final by
+// then) from lane M of the row and subtracts L[i][M] x_M in the lanes i > M.
+template <int M, int N>
+struct TriSolveStep {
+    __device__ __forceinline__ static void run(float& x, const float (&lrow)[16], int l16) {
+        if constexpr (M < N) {
+            const float xm = __int_as_float(
+                __builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + M, 0xF, 0xF, false));  // row_newbcast:M
+            const float nx = fmaf(-lrow[M], xm, x);
+            x = l16 > M ? nx : x;
+            TriSolveStep<M + 1, N>::run(x, lrow, l16);
+        }
+    }
+};
+
+// Row-local shift toward lane 0 by S lanes (lane j takes lane j + S of its
+// DPP row; the last S lanes of the row take `fill`).
+template <int S>
+__device__ __forceinline__ float row_shl(float x, float fill) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x), 0x100 + S, 0xF, 0xF, false));
+}
+
 // Occupancy the register budget is sized for: three 512-thread blocks of the
 // V = 128 kernels per CU, four of the 320-thread V = 80 ones.
 constexpr int kFlushWavesPerEu = 6;
@@ -151,7 +175,7 @@ void flush_kernel(FlushArgs A, HeadTable T) {
     float* Gw = sm + L::gw;
     float* Vw = sm + L::vw;
     float* Kg = sm + L::kg;
-    float* Lt = sm + L::lt;
+    float* Lr = sm + L::lt;
     float* Tm = sm + L::tm;
     float* Al = sm + L::al;
     float* Om = sm + L::om;
@@ -407,51 +431,84 @@ void flush_kernel(FlushArgs A, HeadTable T) {
         __syncthreads();
 
         if (DELTA) {
-            // 4a. L, row i by the 16 lanes of DPP row i (channels 8 l .. 8 l + 7
-            // each), stored transposed: Lt[l][i] = L[i][l]
-            {
+            // 4a. L[i][l] = beta_i sum_c k_i[c] k_l[c] prod_{l<m<=i} alpha_m[c]
+            // (l < i), row-major in Lr.  One DPP row of 16 lanes (channels
+            // 8 l16 .. 8 l16 + 7 each) per entry.
+            if (KDA) {
+                // per-channel decays: row i walks l = i-1 .. 0, one more decay
+                // per step (kd = k_i * prod_{l<m<=i} alpha_m)
                 const int i = tid >> 4;
                 const int l16 = tid & 15;
                 if (i >= 1 && i < W) {
-                    // kd = k_i * prod_{j<m<=i} alpha_m, one more decay per step
                     float kd[8];
                     load8f(Ap + i * KS + 8 * l16, kd);
                     const float bi = pick(bs, i);
                     for (int j = i - 1; j >= 0; --j) {
-                        if (KDA) {
-                            float aj[8];
-                            load8f(Al + (j + 1) * K + 8 * l16, aj);
+                        float aj[8];
+                        load8f(Al + (j + 1) * K + 8 * l16, aj);
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) kd[e] *= aj[e];
-                        } else {
-                            const float aj = pick(as, j + 1);
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) kd[e] *= aj;
-                        }
+                        for (int e = 0; e < 8; ++e) kd[e] *= aj[e];
                         float kj[8];
                         load8f(Ap + j * KS + 8 * l16, kj);
                         const float sum = row_sum16(dot8(kd, kj));
-                        if (l16 == 0) Lt[j * 16 + i] = bi * sum;
+                        if (l16 == 0) Lr[i * 16 + j] = bi * sum;
                     }
+                }
+            } else {
+                // scalar decays: L[i][l] = beta_i P[i][l] (k_i . k_l) with
+                // P[i][l] = prod_{l<m<=i} alpha_m.  First every P[i][l] at
+                // once, DPP row i lane l, as a suffix product over the lanes m > l
+                // of the row (lanes above i contribute 1), with beta_i on the
+                // diagonal; staged in the T area, whose solve comes later.
+                float* Pm = Tm;
+                if (tid < 16 * W) {
+                    const int i = tid >> 4, l = tid & 15;  // lane l holds alpha_l, beta_l
+                    float y = l <= i ? as_l : 1.f;
+                    y *= row_shl<1>(y, 1.f);
+                    y *= row_shl<2>(y, 1.f);
+                    y *= row_shl<4>(y, 1.f);
+                    y *= row_shl<8>(y, 1.f);  // prod_{m >= l, m <= i} alpha_m
+                    const float pl = row_shl<1>(y, 1.f);
+                    Pm[i * 16 + l] = l == i ? bs_l : pl;
+                }
+                __syncthreads();
+                // then the W (W - 1) / 2 entries, spread over all 4 NW rows of
+                // the block, a few per row
+                const int row = tid >> 4;
+                const int l16 = tid & 15;
+                for (int p = row; p < W * (W - 1) / 2; p += 4 * NW) {
+                    // p = i (i - 1) / 2 + j with 0 <= j < i
+                    int i = int((1.f + __builtin_sqrtf(float(1 + 8 * p))) * 0.5f);
+                    i = i * (i - 1) / 2 > p ? i - 1 : i;
+                    i = (i + 1) * i / 2 <= p ? i + 1 : i;
+                    const int j = p - i * (i - 1) / 2;
+                    float ki[8], kj[8];
+                    load8f(Ap + i * KS + 8 * l16, ki);
+                    load8f(Ap + j * KS + 8 * l16, kj);
+                    const float f = Pm[i * 16 + i] * Pm[i * 16 + j];
+                    const float sum = row_sum16(dot8(ki, kj));
+                    if (l16 == 0) Lr[i * 16 + j] = f * sum;
                 }
             }
             __syncthreads();
-            // 4b. T = (I + L)^{-1} diag(beta): lane c of wave 0 solves column c
-            // (column-oriented forward substitution; L is unit-free strictly lower)
-            if (tid < W) {
-                const int c = tid;
-                const float bc = pick(bs, c);
-                float x[W];
+            // 4b. T = (I + L)^{-1} diag(beta) by forward substitution, column c
+            // by DPP row c: lane i holds T[i][c] and L's row i (zero above the
+            // diagonal is never read); lane c starts from beta_c
+            if (tid < 16 * W) {
+                const int c = tid >> 4;
+                const int l16 = tid & 15;
+                float lrow[16];
 #pragma unroll
-                for (int i = 0; i < W; ++i) x[i] = i == c ? bc : 0.f;
-#pragma unroll
-                for (int l = 0; l < W - 1; ++l) {
-                    const float xl = x[l];
-#pragma unroll
-                    for (int i = l + 1; i < W; ++i) x[i] = fmaf(-Lt[l * 16 + i], xl, x[i]);
+                for (int q = 0; q < 4; ++q) {
+                    const float4 v4 = *reinterpret_cast<const float4*>(Lr + l16 * 16 + 4 * q);
+                    lrow[4 * q] = v4.x;
+                    lrow[4 * q + 1] = v4.y;
+                    lrow[4 * q + 2] = v4.z;
+                    lrow[4 * q + 3] = v4.w;
                 }
-#pragma unroll
-                for (int i = 0; i < W; ++i) Tm[i * 16 + c] = x[i];
+                float x = l16 == c ? bs_l : 0.f;
+                TriSolveStep<0, W - 1>::run(x, lrow, l16);
+                Tm[l16 * 16 + c] = x;
             }
             __syncthreads();
             // 4c. u = T V_w on this wave's columns, and -T (gamma K) over all keys
