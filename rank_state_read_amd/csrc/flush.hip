@@ -109,20 +109,6 @@ __device__ __forceinline__ float quarter_sum4(float x) {
     return x;
 }
 
-__device__ __forceinline__ float read_lane(float x, int l) {
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
-}
-
-// x[i] for a lane-dependent i (a select chain; x is wave-uniform).
-template <int N>
-__device__ __forceinline__ float pick(const float (&x)[N], int i) {
-    float r = 0.f;
-#pragma unroll
-    for (int j = 0; j < N; ++j)
-        if (j == i) r = x[j];
-    return r;
-}
-
 // One column of the unit lower-triangular solve (I + L) x = b held by a DPP
 // row, lane i holding x_i and its row of L: step M broadcasts x_M (final by
 // then) from lane M of the row and subtracts L[i][M] x_M in the lanes i > M.
@@ -140,11 +126,16 @@ struct TriSolveStep {
 };
 
 // Row-local shift toward lane 0 by S lanes (lane j takes lane j + S of its
-// DPP row; the last S lanes of the row take `fill`).
+// DPP row; the last S lanes of the row take `fill`), and toward lane 15.
 template <int S>
 __device__ __forceinline__ float row_shl(float x, float fill) {
     return __int_as_float(
         __builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x), 0x100 + S, 0xF, 0xF, false));
+}
+template <int S>
+__device__ __forceinline__ float row_shr(float x, float fill) {
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(x), 0x110 + S, 0xF, 0xF, false));
 }
 
 // Occupancy the register budget is sized for: three 512-thread blocks of the
@@ -340,14 +331,9 @@ void flush_kernel(FlushArgs A, HeadTable T) {
 
     // ---- 4. window-only work while the state is in flight ----
     // slots >= n act as alpha = 1, beta = 0, k = v = 0
+    // (lane l of every DPP row holds slot l's scalar decay and beta)
     as_l = (lane & 15) < n ? as_l : 1.f;
     bs_l = (lane & 15) < n ? bs_l : 0.f;
-    float as[W], bs[W];
-#pragma unroll
-    for (int i = 0; i < W; ++i) {
-        as[i] = read_lane(as_l, i);
-        bs[i] = read_lane(bs_l, i);
-    }
     float gamW = 1.f;
     f32x4 u = {0.f, 0.f, 0.f, 0.f};
     float zc = 0.f;     // fused: sum_m c_m Z_old[m][column], this lane's column
@@ -402,16 +388,25 @@ void flush_kernel(FlushArgs A, HeadTable T) {
                 }
             }
         } else {
-            // scalar decays: this thread's slot's prefix / suffix products
-#pragma unroll
-            for (int i = 0; i < W; ++i) gamW *= as[i];
+            // scalar decays: gamma_l = prod_{m<=l} alpha_m and sigma_l =
+            // prod_{m>l} alpha_m for every slot at once (lane l of each DPP row
+            // holds alpha_l: a prefix and a suffix product over the row); each
+            // key chunk then takes its slot's pair from lane ki of its row
+            float gam = as_l, sig = as_l;
+            gam *= row_shr<1>(gam, 1.f);
+            gam *= row_shr<2>(gam, 1.f);
+            gam *= row_shr<4>(gam, 1.f);
+            gam *= row_shr<8>(gam, 1.f);
+            sig *= row_shl<1>(sig, 1.f);
+            sig *= row_shl<2>(sig, 1.f);
+            sig *= row_shl<4>(sig, 1.f);
+            sig *= row_shl<8>(sig, 1.f);
+            sig = row_shl<1>(sig, 1.f);
+            gamW = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(gam), 0x150 + W - 1, 0xF, 0xF,
+                                                              false));  // row_newbcast:15
             if (tid < KCH) {
-                float gi = 1.f, si = 1.f;
-#pragma unroll
-                for (int i = 0; i < W; ++i) {
-                    if (i <= ki) gi *= as[i];
-                    if (i > ki) si *= as[i];
-                }
+                const float gi = __shfl(gam, ki, 16);
+                const float si = __shfl(sig, ki, 16);
                 float f[8], t[8];
                 V8::unpack(kraw, f);
 #pragma unroll
@@ -442,7 +437,7 @@ void flush_kernel(FlushArgs A, HeadTable T) {
                 if (i >= 1 && i < W) {
                     float kd[8];
                     load8f(Ap + i * KS + 8 * l16, kd);
-                    const float bi = pick(bs, i);
+                    const float bi = __shfl(bs_l, i, 16);
                     for (int j = i - 1; j >= 0; --j) {
                         float aj[8];
                         load8f(Al + (j + 1) * K + 8 * l16, aj);
