@@ -224,6 +224,23 @@ void flush_kernel(FlushArgs A, HeadTable T) {
         }
     };
 
+    // The state is requested after the window (below), except in the fused
+    // Mamba-2 pass, whose window-phase work (the last token's read) is short:
+    // there it goes first and that work waits for it (641 against 649 us at a
+    // Nano-shaped layer; for the other instances this order measured the same
+    // or slower).
+    constexpr bool SFIRST = FUSED && KIND == SKSSM_MAMBA2;
+    const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(A.S + item * size_t(K) * V, K * V * 4);
+    const int svo = (4 * lq * V + v0 + lr) * 4;  // this lane's byte offset in a 16-row tile
+    f32x4 s[8];
+    auto load_state = [&]() {
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) s[kt][rr] = buffer_load_f32(srs, svo, (16 * kt + rr) * V * 4);
+    };
+    if (SFIRST) load_state();
+
     // ---- 1. window loads into registers, issued first ----
     // Every slot is fetched (the window always holds W slots) and slots >= n
     // are masked where the values are used: the loads then need no branches,
@@ -321,16 +338,11 @@ void flush_kernel(FlushArgs A, HeadTable T) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
     // ---- 3. the state: this wave's 16 columns, all key rows ----
-    const __amdgpu_buffer_rsrc_t srs = buffer_rsrc(A.S + item * size_t(K) * V, K * V * 4);
-    const int svo = (4 * lq * V + v0 + lr) * 4;  // this lane's byte offset in a 16-row tile
-    f32x4 s[8];
-#pragma unroll
-    for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) s[kt][rr] = buffer_load_f32(srs, svo, (16 * kt + rr) * V * 4);
+    if (!SFIRST) load_state();
 
     // ---- 4. window-only work while the state is in flight ----
     // slots >= n act as alpha = 1, beta = 0, k = v = 0
+    if (SFIRST) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the state landed with the window
     // (lane l of every DPP row holds slot l's scalar decay and beta)
     as_l = (lane & 15) < n ? as_l : 1.f;
     bs_l = (lane & 15) < n ? bs_l : 0.f;
