@@ -443,14 +443,33 @@ void flush_kernel(FlushArgs A, HeadTable T) {
             // 8 l16 .. 8 l16 + 7 each) per entry.
             if (KDA) {
                 // per-channel decays: row i walks l = i-1 .. 0, one more decay
-                // per step (kd = k_i * prod_{l<m<=i} alpha_m)
-                const int i = tid >> 4;
+                // per step (kd = k_i * prod_{l<m<=i} alpha_m).  With 32 DPP rows
+                // or more the walk is split: row i takes l = i-1 .. i/2, row
+                // W + i first applies the decays of slots i .. i/2 + 1 (cheap:
+                // no sums) and then takes l = i/2 - 1 .. 0, so no row sums more
+                // than eight entries; the products are formed in the same order.
+                constexpr bool SPLIT = 4 * NW >= 2 * W;
+                const int R = tid >> 4;
                 const int l16 = tid & 15;
-                if (i >= 1 && i < W) {
+                const int i = SPLIT ? (R & (W - 1)) : R;
+                const bool lower = SPLIT && R >= W;
+                if (R < (SPLIT ? 2 * W : W) && i >= 1) {
+                    const int h = SPLIT ? i / 2 : 0;
                     float kd[8];
                     load8f(Ap + i * KS + 8 * l16, kd);
                     const float bi = __shfl(bs_l, i, 16);
-                    for (int j = i - 1; j >= 0; --j) {
+                    int jhi = i - 1, jlo = h;
+                    if (lower) {
+                        for (int m = i; m > h; --m) {
+                            float am[8];
+                            load8f(Al + m * K + 8 * l16, am);
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) kd[e] *= am[e];
+                        }
+                        jhi = h - 1;
+                        jlo = 0;
+                    }
+                    for (int j = jhi; j >= jlo; --j) {
                         float aj[8];
                         load8f(Al + (j + 1) * K + 8 * l16, aj);
 #pragma unroll
