@@ -261,6 +261,9 @@ def main():
                     help="calibration file whose per-layer basis replaces the synthetic one (layer i uses basis i)")
     ap.add_argument("--kq-heads", type=int, default=0,
                     help="share q and k among H / N consecutive heads (grouped keys and queries)")
+    ap.add_argument("--launch-order", default="bucket", choices=("bucket", "head", "low-first"),
+                    help="launch order of the sketch heads: the planner's rank buckets from high to low "
+                         "(default), head order, or buckets from low to high")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="only the warmup and timed decode steps (for counter runs)")
@@ -287,7 +290,7 @@ def main():
         return
 
     from rank_state_read_amd import binding as Bnd
-    from rank_state_read_amd.layer import layer_for_workload
+    from rank_state_read_amd.layer import launch_order, layer_for_workload
     from workloads import CONFIGS, Workload
 
     def log(msg):
@@ -312,16 +315,18 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    # the planner's own order unless another is asked for
+    order = None if args.launch_order == "bucket" else launch_order(wl.ranks, args.launch_order)
     t0 = time.time()
-    lay0 = layer_for_workload(wl, device=dev)
+    lay0 = layer_for_workload(wl, device=dev, order=order)
     log(f"state generated ({time.time() - t0:.1f}s)")
     if cal is not None:
         lay0 = layer_for_workload(Workload(cfg, ranks=wl.ranks, basis=cal["omega"][0]), device=dev,
-                                  S_init=lay0.S)
+                                  S_init=lay0.S, order=order)
     lays = [lay0]
     for i in range(1, NI):
         wli = wl if cal is None else Workload(cfg, ranks=wl.ranks, basis=cal["omega"][i % len(cal["omega"])])
-        lays.append(layer_for_workload(wli, device=dev, S_init=lay0.S))
+        lays.append(layer_for_workload(wli, device=dev, S_init=lay0.S, order=order))
     host_steps = [wl.step(t) for t in range(W)]
     inputs0 = [lay0.upload_step(st) for st in host_steps]
 
@@ -529,10 +534,12 @@ def main():
         "hbm_GBps": round(sb / (us_step * 1e3), 1),
         "config": {"workload": workload_name(cfg, ranks),
                    "global_batch": cfg.B, "layer_instances": NI, "parallelism": "none (1 GPU)",
-                   **({"basis": f"calibration file, layers {cal['layer_ids'][:NI]}"} if cal is not None else {})},
+                   **({"basis": f"calibration file, layers {cal['layer_ids'][:NI]}"} if cal is not None else {}),
+                   **({"launch_order": args.launch_order} if order is not None else {})},
         "roofline": {"bound": "hbm", "kernel": "read_kernel (sketchssm_decode_read)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(cfg.name),
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(cfg.name) if order is None else None,
                      "bytes_per_launch": int(rb_avg), "avg_launch_us": round(read_us, 3),
                      "ceiling_GBps": ceil["mix_GBps"], "ceiling": ceil["mix_desc"],
                      "frac_of_ceiling": round(achieved / ceil["mix_GBps"], 4)},

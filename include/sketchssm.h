@@ -110,6 +110,20 @@ sketchssm_status sketchssm_plan_create(const sketchssm_shape* shape, const int32
                                        const int32_t* group, sketchssm_plan** out);
 
 /*
+ * Host only.  As sketchssm_plan_create, with the launch order given instead of
+ * derived (the pages fix no order; this serves to compare orders, e.g. head
+ * order against the rank buckets):
+ *   order[H] : a permutation of 0..H-1 listing every dense head (rank 0) before
+ *              any sketch head; copied.
+ * Frames, offsets and buckets are those of sketchssm_plan_create; only the
+ * launch order differs, and no result depends on it (every item is computed
+ * the same way in any order).  SKSSM_ESHAPE if order is not such a permutation.
+ */
+sketchssm_status sketchssm_plan_create_ordered(const sketchssm_shape* shape, const int32_t* rank,
+                                               const int32_t* group, const int32_t* order,
+                                               sketchssm_plan** out);
+
+/*
  * Host only.  Copies the derived tables into caller arrays (any may be NULL):
  *   frame_index[H]    frame of each head, -1 for a dense head
  *   frame_row_off[F+1] first row of each frame in the frames array

@@ -42,6 +42,8 @@ _lib = None
 
 _PROTOS = {
     "sketchssm_plan_create": (c_i32, [ctypes.POINTER(Shape), c_i32p, c_i32p, ctypes.POINTER(c_vp)]),
+    "sketchssm_plan_create_ordered": (c_i32, [ctypes.POINTER(Shape), c_i32p, c_i32p, c_i32p,
+                                              ctypes.POINTER(c_vp)]),
     "sketchssm_plan_export": (c_i32, [c_vp] + [c_i32p] * 8),
     "sketchssm_plan_destroy": (None, [c_vp]),
     "sketchssm_z_elems": (ctypes.c_size_t, [c_vp]),
@@ -113,16 +115,25 @@ def _stream(stream):
 class Plan:
     """Owner of a ``sketchssm_plan`` (host only)."""
 
-    def __init__(self, shape: Shape, rank, group):
+    def __init__(self, shape: Shape, rank, group, order=None):
         self.shape = shape
         r = np.ascontiguousarray(rank, dtype=np.int32)
         g = np.ascontiguousarray(group, dtype=np.int32)
         if shape.H >= 1 and (r.shape != (shape.H,) or g.shape != (shape.H,)):
             raise ValueError("rank and group must have H entries")
         h = c_vp()
-        _check("sketchssm_plan_create",
-               lib().sketchssm_plan_create(ctypes.byref(shape), r.ctypes.data_as(c_i32p),
-                                           g.ctypes.data_as(c_i32p), ctypes.byref(h)))
+        if order is None:
+            _check("sketchssm_plan_create",
+                   lib().sketchssm_plan_create(ctypes.byref(shape), r.ctypes.data_as(c_i32p),
+                                               g.ctypes.data_as(c_i32p), ctypes.byref(h)))
+        else:
+            o = np.ascontiguousarray(order, dtype=np.int32)
+            if o.shape != (shape.H,):
+                raise ValueError("order must have H entries")
+            _check("sketchssm_plan_create_ordered",
+                   lib().sketchssm_plan_create_ordered(ctypes.byref(shape), r.ctypes.data_as(c_i32p),
+                                                       g.ctypes.data_as(c_i32p), o.ctypes.data_as(c_i32p),
+                                                       ctypes.byref(h)))
         self.handle = h.value
         self.rank = r.copy()
         self.group = g.copy()

@@ -47,8 +47,11 @@ void dense_table(const sketchssm_shape& s, HeadTable* t) {
 
 using namespace skssm;
 
-extern "C" sketchssm_status sketchssm_plan_create(const sketchssm_shape* shape, const int32_t* rank,
-                                                  const int32_t* group, sketchssm_plan** out) {
+// The plan of a rank table; `order` (may be null) replaces the derived launch
+// order: a permutation of 0..H-1 that lists every dense head before any sketch
+// head (the read kernel's blocks take the dense heads first).
+static sketchssm_status make_plan(const sketchssm_shape* shape, const int32_t* rank,
+                                  const int32_t* group, const int32_t* order, sketchssm_plan** out) {
     if (!out) return SKSSM_EINVAL;
     *out = nullptr;
     if (!rank || !group) return SKSSM_EINVAL;
@@ -92,14 +95,18 @@ extern "C" sketchssm_status sketchssm_plan_create(const sketchssm_shape* shape, 
             p->max_rank = std::max(p->max_rank, rank[h]);
         }
         p->order.resize(H);
-        for (int h = 0; h < H; ++h) p->order[h] = h;
-        const std::vector<int32_t>& bk = p->bucket;
-        std::stable_sort(p->order.begin(), p->order.end(), [&](int32_t x, int32_t y) {
-            const bool dx = bk[x] == 0, dy = bk[y] == 0;
-            if (dx != dy) return dx;          // dense first
-            if (bk[x] != bk[y]) return bk[x] > bk[y];
-            return x < y;
-        });
+        if (order) {
+            p->order.assign(order, order + H);
+        } else {
+            for (int h = 0; h < H; ++h) p->order[h] = h;
+            const std::vector<int32_t>& bk = p->bucket;
+            std::stable_sort(p->order.begin(), p->order.end(), [&](int32_t x, int32_t y) {
+                const bool dx = bk[x] == 0, dy = bk[y] == 0;
+                if (dx != dy) return dx;          // dense first
+                if (bk[x] != bk[y]) return bk[x] > bk[y];
+                return x < y;
+            });
+        }
         p->n_dense = 0;
         for (int h = 0; h < H; ++h) p->n_dense += (rank[h] == 0);
         p->z_elems = size_t(shape->B) * shape->V * size_t(p->z_row_off.back());
@@ -120,6 +127,32 @@ extern "C" sketchssm_status sketchssm_plan_create(const sketchssm_shape* shape, 
     }
     *out = p;
     return SKSSM_OK;
+}
+
+extern "C" sketchssm_status sketchssm_plan_create(const sketchssm_shape* shape, const int32_t* rank,
+                                                  const int32_t* group, sketchssm_plan** out) {
+    return make_plan(shape, rank, group, nullptr, out);
+}
+
+extern "C" sketchssm_status sketchssm_plan_create_ordered(const sketchssm_shape* shape,
+                                                          const int32_t* rank, const int32_t* group,
+                                                          const int32_t* order, sketchssm_plan** out) {
+    if (!out) return SKSSM_EINVAL;
+    *out = nullptr;
+    if (!order || !rank) return SKSSM_EINVAL;
+    const sketchssm_status st = check_shape(shape);
+    if (st != SKSSM_OK) return st;
+    const int H = shape->H;
+    std::vector<char> seen(H, 0);
+    bool sketch_seen = false;
+    for (int i = 0; i < H; ++i) {
+        const int h = order[i];
+        if (h < 0 || h >= H || seen[h]) return SKSSM_ESHAPE;  // not a permutation
+        seen[h] = 1;
+        if (rank[h] > 0) sketch_seen = true;
+        else if (sketch_seen) return SKSSM_ESHAPE;  // a dense head after a sketch head
+    }
+    return make_plan(shape, rank, group, order, out);
 }
 
 extern "C" sketchssm_status sketchssm_plan_export(const sketchssm_plan* p, int32_t* frame_index,

@@ -38,13 +38,14 @@ class SketchLayer:
 
     def __init__(self, *, B: int, H: int, K: int, V: int, W: int, G: int, basis_rows: int,
                  rank_cap: int, kind: str, qkv: str, rank, group, basis,
-                 fmap: Optional[Callable] = None, S_init=None, device="cuda", kq_heads: int = 0):
+                 fmap: Optional[Callable] = None, S_init=None, device="cuda", kq_heads: int = 0,
+                 order=None):
         self.kind, self.qkv = kind, qkv
         self.B, self.H, self.K, self.V, self.W = B, H, K, V, W
         self.Hk = int(kq_heads) if kq_heads else H
         self.device = torch.device(device)
         self.shape = _shape(B, H, K, V, W, G, basis_rows, rank_cap, kind, qkv, kq_heads)
-        self.plan = _plan(self.shape, rank, group)
+        self.plan = _plan(self.shape, rank, group, order)
         self.layout = self.plan.export()
         dev = self.device
         self.S = torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
@@ -150,18 +151,40 @@ def _shape(B_, H, K, V, W, G, basis_rows, rank_cap, kind, qkv, kq_heads=0):
     return _b.make_shape(B_, H, K, V, W, G, basis_rows, rank_cap, kind, qkv, kq_heads)
 
 
-def _plan(shape, rank, group):
-    return _b.Plan(shape, rank, group)
+def _plan(shape, rank, group, order=None):
+    return _b.Plan(shape, rank, group, order)
 
 
-def layer_for_workload(wl, *, ranks=None, device="cuda", S_init=None, with_state=True) -> SketchLayer:
-    """A SketchLayer for a ``workloads.Workload`` (ranks may be overridden, e.g. all zero)."""
+def launch_order(rank, kind: str = "bucket"):
+    """A launch order for ``sketchssm_plan_create_ordered``: dense heads first
+    (ascending), then the sketch heads in head order ("head"), by rank bucket
+    from low to high ("low-first"), or from high to low ("bucket", the
+    planner's own order)."""
+    rank = np.asarray(rank, np.int64)
+    dense = [h for h in range(len(rank)) if rank[h] == 0]
+    sk = [h for h in range(len(rank)) if rank[h] > 0]
+    bucket = {h: 1 + (int(rank[h]) - 1) // 8 for h in sk}
+    if kind == "head":
+        pass
+    elif kind == "low-first":
+        sk.sort(key=lambda h: (bucket[h], h))
+    elif kind == "bucket":
+        sk.sort(key=lambda h: (-bucket[h], h))
+    else:
+        raise ValueError(f"unknown launch order {kind!r}")
+    return np.array(dense + sk, np.int32)
+
+
+def layer_for_workload(wl, *, ranks=None, device="cuda", S_init=None, with_state=True,
+                       order=None) -> SketchLayer:
+    """A SketchLayer for a ``workloads.Workload`` (ranks may be overridden, e.g.
+    all zero; ``order``: an explicit launch order, see ``launch_order``)."""
     c = wl.cfg
     rk = wl.ranks if ranks is None else np.asarray(ranks, np.int32)
     lay = SketchLayer(B=c.B, H=c.H, K=c.K, V=c.V, W=c.W, G=c.G, basis_rows=c.basis_rows,
                       rank_cap=c.rank_cap, kind=c.kind, qkv=c.qkv, rank=rk, group=wl.groups,
                       basis=wl.basis, fmap=wl.fmap, S_init=None, device=device,
-                      kq_heads=c.kq_heads or 0)
+                      kq_heads=c.kq_heads or 0, order=order)
     if S_init is not None:
         lay.S.copy_(_to_device(S_init, torch.float32, lay.device))
     elif with_state:

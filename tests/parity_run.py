@@ -34,7 +34,7 @@ class Run:
     """Drive one layer on the GPU and the oracle on a set of (b, h) items."""
 
     def __init__(self, wl, items=None, dense_baseline=False, step_source=None, z_error_bound=False,
-                 fused=False, fill_state=None):
+                 fused=False, fill_state=None, order=None):
         from rank_state_read_amd.layer import layer_for_workload
         self.wl = wl
         c = wl.cfg
@@ -43,7 +43,7 @@ class Run:
         self.src = step_source or wl
         # fill_state(S): writes the initial state into the device tensor instead
         # of the workload's own draw
-        self.lay = layer_for_workload(wl, with_state=fill_state is None)
+        self.lay = layer_for_workload(wl, with_state=fill_state is None, order=order)
         if fill_state is not None:
             fill_state(self.lay.S)
         self.items = items if items is not None else [(b, h) for b in range(c.B) for h in range(c.H)]

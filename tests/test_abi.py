@@ -72,6 +72,39 @@ def test_plan_hand_example_from_library(golden_dir):
         assert got[key].tolist() == g[key], key
 
 
+def test_plan_with_explicit_order():
+    """sketchssm_plan_create_ordered: the given order, every other table as the
+    derived plan's; a non-permutation or a dense head after a sketch head is
+    refused."""
+    from rank_state_read_amd.layer import launch_order
+    rng = np.random.default_rng(5)
+    for trial in range(100):
+        H = int(rng.integers(1, 257))
+        G = int(rng.integers(1, 9))
+        rank = rng.integers(0, 50, size=H).astype(np.int32)
+        rank[rng.random(H) < 0.2] = 0
+        group = rng.integers(0, G, size=H).astype(np.int32)
+        sh = _shape(H=H, G=G)
+        base = B.Plan(sh, rank, group).export()
+        for kind in ("bucket", "head", "low-first"):
+            o = launch_order(rank, kind)
+            got = B.Plan(sh, rank, group, o).export()
+            assert np.array_equal(got["order"], o)
+            for key in ("frame_index", "frame_row_off", "z_row_off", "bucket"):
+                assert np.array_equal(got[key], base[key]), (trial, kind, key)
+            assert got["frames"] == base["frames"]
+        # the planner's own order is the "bucket" order
+        assert np.array_equal(launch_order(rank, "bucket"), base["order"])
+    sh = _shape(H=4, G=1)
+    rank = np.array([0, 3, 5, 0], np.int32)
+    group = np.zeros(4, np.int32)
+    for bad in ([0, 1, 2, 2], [0, 1, 2, 4], [0, 1, 3, 2], [1, 0, 3, 2]):
+        with pytest.raises(RuntimeError, match="ESHAPE"):
+            B.Plan(sh, rank, group, np.array(bad, np.int32))
+    ok = B.Plan(sh, rank, group, np.array([3, 0, 2, 1], np.int32)).export()
+    assert ok["order"].tolist() == [3, 0, 2, 1]
+
+
 @pytest.mark.parametrize("bad", [
     dict(H=0), dict(H=257), dict(V=72), dict(V=48), dict(V=144), dict(G=0), dict(cap=65), dict(B_=0),
     dict(kq=3), dict(kq=16), dict(kq=-1),

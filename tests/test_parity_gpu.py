@@ -98,6 +98,22 @@ def test_dense_read_baseline(name, B):
     _run_steps(wl0, 2 * cfg.W + 3, dense_baseline=True, step_source=wl)
 
 
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name,B", [("c1", 20), ("c4", 19)])
+@pytest.mark.parametrize("kind", ["head", "low-first"])
+def test_other_launch_orders(name, B, kind):
+    """A plan made with sketchssm_plan_create_ordered: the oracle's outputs, and
+    bit for bit those of the planner's own order (no item depends on the order)."""
+    import torch
+    from rank_state_read_amd.layer import launch_order
+    wl = Workload(CONFIGS[name].with_batch(B))
+    steps = wl.cfg.W + 3
+    ref = _run_steps(wl, steps, fused=True)
+    got = _run_steps(wl, steps, fused=True, order=launch_order(wl.ranks, kind))
+    assert torch.equal(got.lay.S, ref.lay.S) and torch.equal(got.lay.Z, ref.lay.Z)
+    assert torch.equal(got.lay.y, ref.lay.y)
+
+
 # ---------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------
