@@ -53,6 +53,33 @@ int main(void) {
     sh.V = 72;
     printf("bad_V %d\n", (int)sketchssm_plan_create(&sh, rank, group, &plan));
     sh.V = 80;
+    {
+        /* an explicit launch order: the planner's own, reversed among the sketch
+           heads, is accepted; a dense head placed after a sketch head is not */
+        int32_t ord[8], i, nd = 0, ns = 0;
+        int32_t dense_idx[8], sketch_idx[8];
+        for (i = 0; i < 8; ++i) {
+            if (rank[order[i]] == 0) dense_idx[nd++] = order[i];
+            else sketch_idx[ns++] = order[i];
+        }
+        for (i = 0; i < nd; ++i) ord[i] = dense_idx[i];
+        for (i = 0; i < ns; ++i) ord[nd + i] = sketch_idx[ns - 1 - i];
+        st = sketchssm_plan_create_ordered(&sh, rank, group, ord, &plan);
+        if (st == SKSSM_OK) {
+            int32_t got[8];
+            sketchssm_plan_export(plan, NULL, NULL, NULL, NULL, got, NULL, NULL, NULL);
+            print_row("ordered", got, 8);
+            sketchssm_plan_destroy(plan);
+            plan = NULL;
+        }
+        printf("ordered_status %d\n", (int)st);
+        if (nd > 0 && ns > 0) {
+            int32_t t = ord[0];
+            ord[0] = ord[7];
+            ord[7] = t;
+            printf("ordered_dense_late %d\n", (int)sketchssm_plan_create_ordered(&sh, rank, group, ord, &plan));
+        }
+    }
     printf("flush_null_plan %d\n", (int)sketchssm_flush(NULL, NULL, NULL, NULL, NULL, NULL, NULL,
                                                         NULL, 0, NULL));
     printf("probe_null %d\n", (int)sketchssm_stream_probe(NULL, 4096 * 8, NULL, 0, 8, 1, 0, NULL));

@@ -41,6 +41,12 @@ def test_c_client(tmp_path, golden_dir):
     assert int(out["frame_elems"]) == 128 * sum(r for _, r in g["frames"])
     assert int(out["null_out"]) == 1      # SKSSM_EINVAL
     assert int(out["bad_V"]) == 2         # SKSSM_ESHAPE
+    assert int(out["ordered_status"]) == 0
+    o = list(g["order"])
+    dense = [h for h in o if g["rank"][h] == 0]
+    sk = [h for h in o if g["rank"][h] > 0]
+    assert ints(out["ordered"]) == dense + sk[::-1]
+    assert int(out["ordered_dense_late"]) == 2   # a dense head after a sketch head
     assert int(out["flush_null_plan"]) == 1
     assert int(out["probe_null"]) == 1    # SKSSM_EINVAL
     assert "aligned" in out["status_text"]
