@@ -280,3 +280,14 @@ def test_stream_probe_argument_errors():
     assert probe(a16, 8 * 4096, a16, 0, 8, 0, 0, None) == 1             # read-only needs a bounded grid
     assert probe(a16, 8 * 4096, a16, 0, 8, -1, 0, None) == 1            # negative grid
     assert probe(a16, 8 * 4096, a16, 0, 8, 4, 2, None) == 1             # unknown flag
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """With the HIP library absent every entry point raises: there is no
+    fallback path."""
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "libsketchssm.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        B.Plan(_shape(), np.zeros(8, np.int32), np.zeros(8, np.int32))
