@@ -103,6 +103,12 @@ def read_bytes(cfg, ranks, pos: int, dense_all: bool = False) -> int:
     return total
 
 
+def read_write_bytes(cfg) -> int:
+    """The part of a read launch's bytes that it writes: y and the appended
+    token of every item (the same at every window position)."""
+    return int(cfg.B * cfg.H * (cfg.V * 4 + token_bytes(cfg)))
+
+
 def flush_bytes(cfg, ranks, n_tokens: int, dense_all: bool = False) -> int:
     total = 0
     for h in range(cfg.H):
@@ -196,40 +202,60 @@ STREAM_BYTES = 1 << 30
 MIX_READS_PER_WRITE = 8
 
 
-def stream_ceilings(torch, Bnd, timed, dev) -> dict:
+def stream_ceilings(torch, Bnd, timed, dev, launches=()) -> dict:
     """Best rate (read + written bytes per second) of the streaming probe for
     an 8:1 read:write mix, for reads alone and for a 1:1 copy, each the best
     of a few launch shapes; and torch's device-to-device copy for reference.
 
+    launches: (bytes, written bytes) of kernel launches to match.  For each,
+    the probe also streams a launch of the same size at the nearest mix it
+    offers (2, 4, 8 or 16 reads per write) and the result gives the time a
+    plain stream of that size and mix takes for the launch's bytes: the fixed
+    cost of filling and draining the chip is then in both times, so the ratio
+    shows what the kernel loses beyond it.
+
     Like the decode kernels, which rotate over layer instances, the probe
     never finds its data in the 256 MB last-level cache: successive launches
-    read the two 1 GiB sources in turn and write successive parts of a 2 GiB
+    read the two 1 GiB sources in turn (a launch smaller than a source reads
+    the next of its disjoint regions) and write successive parts of a 2 GiB
     destination pool (the 128 MB written by one 8:1 launch would otherwise
     stay in that cache from one launch to the next)."""
     srcs = [torch.ones(STREAM_BYTES // 4, dtype=torch.float32, device=dev) for _ in range(2)]
     pool = torch.empty(2 * STREAM_BYTES // 4, dtype=torch.float32, device=dev)
     turn = [0]
 
-    def launch(write_bytes, unroll, blocks, nt):
+    def launch(write_bytes, unroll, blocks, nt, read_bytes=STREAM_BYTES):
         i = turn[0]
         turn[0] += 1
+        regions = STREAM_BYTES // read_bytes   # disjoint regions per source
+        src = srcs[i % 2][(i // 2) % regions * (read_bytes // 4):]
         span = max(write_bytes, 4096 * max(blocks, 1))  # bytes this launch writes
         slot = i % max(1, pool.numel() * 4 // span)
         dst = pool[slot * span // 4:]
-        Bnd.sketchssm_stream_probe(srcs[i % 2], STREAM_BYTES, dst, write_bytes, unroll, blocks, nt)
+        Bnd.sketchssm_stream_probe(src, read_bytes, dst, write_bytes, unroll, blocks, nt)
 
-    def rate(write_bytes, unroll, blocks, nt):
-        f = lambda: launch(write_bytes, unroll, blocks, nt)  # noqa: E731
+    def rate(write_bytes, unroll, blocks, nt, read_bytes=STREAM_BYTES):
+        f = lambda: launch(write_bytes, unroll, blocks, nt, read_bytes)  # noqa: E731
         f()
         us = timed(f, reps=6) * 1000.0
-        return (STREAM_BYTES + write_bytes) / (us * 1e3)
+        return (read_bytes + write_bytes) / (us * 1e3)
 
-    def best(write_bytes, shapes):
-        return max((rate(write_bytes, u, b, nt), u, b, nt) for u, b in shapes for nt in (False, True))
+    def best(write_bytes, shapes, read_bytes=STREAM_BYTES):
+        return max((rate(write_bytes, u, b, nt, read_bytes), u, b, nt) for u, b in shapes for nt in (False, True))
 
     mix = best(STREAM_BYTES // MIX_READS_PER_WRITE, [(8, 0), (16, 0), (8, 2048), (16, 2048)])
     ro = best(0, [(4, 1024), (8, 1024), (8, 2048), (16, 1024), (16, 2048)])
     cp = best(STREAM_BYTES, [(4, 0), (8, 0), (8, 4096)])
+    matched_us, matched_mix = [], []
+    chunk = 16 * 4096          # whole chunks for either unroll
+    for nbytes, wbytes in launches:
+        reads = nbytes - wbytes
+        m = min((2, 4, 8, 16), key=lambda x: abs(np.log2(x) - np.log2(max(reads, 1) / max(wbytes, 1))))
+        rd = max(chunk, int(round(reads / chunk)) * chunk)
+        shapes = [(16, 0)] + ([(8, 0)] if m <= 8 else [])
+        r_best = best(rd // m, shapes, rd)
+        matched_us.append(nbytes / (r_best[0] * 1e3))   # the launch's bytes at the probe's rate
+        matched_mix.append(m)
     half = srcs[0][: STREAM_BYTES // 8]      # 512 MB, twice the Infinity Cache
     other = pool[: STREAM_BYTES // 8]
     other.copy_(half)
@@ -239,7 +265,8 @@ def stream_ceilings(torch, Bnd, timed, dev) -> dict:
                        f"unroll {mix[1]}, {'one block per chunk' if mix[2] == 0 else f'{mix[2]} blocks'}, "
                        f"{'non-temporal' if mix[3] else 'plain'} loads and stores)",
            "read_only_GBps": round(ro[0], 1), "copy_GBps": round(cp[0], 1),
-           "torch_copy_GBps": round(2 * half.numel() * 4 / (tc_us * 1e3), 1)}
+           "torch_copy_GBps": round(2 * half.numel() * 4 / (tc_us * 1e3), 1),
+           "matched_us": matched_us, "matched_mix": matched_mix}
     del srcs, pool, half, other
     torch.cuda.empty_cache()
     return out
@@ -508,10 +535,10 @@ def main():
     rmw_us = timed(lambda: [rmw(L, p) for p in range(W) for L in lays], reps=2) * 1000.0 / (NI * W)
 
     # ---- practical HBM ceilings on this GPU, measured in the same run --------
-    ceil = stream_ceilings(torch, Bnd, timed, dev)
-
     ranks = wl.ranks
     rb = [read_bytes(cfg, ranks, p) for p in range(W)]
+    ceil = stream_ceilings(torch, Bnd, timed, dev, launches=[(b, read_write_bytes(cfg)) for b in rb])
+    matched_us = float(np.mean(ceil["matched_us"]))
     read_GBps = float(np.mean([b / (t * 1e3) for b, t in zip(rb, per_pos)]))
     rb_avg = float(np.mean(rb))
     fb = flush_bytes(cfg, ranks, W)
@@ -542,11 +569,17 @@ def main():
                      "traffic": measured_traffic(cfg.name) if order is None else None,
                      "bytes_per_launch": int(rb_avg), "avg_launch_us": round(read_us, 3),
                      "ceiling_GBps": ceil["mix_GBps"], "ceiling": ceil["mix_desc"],
-                     "frac_of_ceiling": round(achieved / ceil["mix_GBps"], 4)},
+                     "frac_of_ceiling": round(achieved / ceil["mix_GBps"], 4),
+                     "ceiling_matched_GBps": round(rb_avg / (matched_us * 1e3), 1),
+                     "ceiling_matched": "streaming probe launches of each window position's read size and nearest "
+                                        "read:write mix (2, 4, 8 or 16:1), rotating buffers",
+                     "frac_of_matched_ceiling": round(matched_us / read_us, 4)},
         "detail": {
             "read_us_mean": round(read_us, 3),
             "read_us_per_pos": [round(x, 2) for x in per_pos],
             "read_GBps": round(read_GBps, 1),
+            "stream_matched_us_per_pos": [round(x, 2) for x in ceil["matched_us"]],
+            "stream_matched_mix_per_pos": ceil["matched_mix"],
             "flush_us": round(flush_us, 2),
             "flush_GBps": round(fb / (flush_us * 1e3), 1),
             "initial_sketch_us": round(init_us, 2),

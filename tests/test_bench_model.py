@@ -62,6 +62,15 @@ def test_standard_decode_bytes_at_the_nano_layer():
     assert bench.rmw_bytes(cfg) == cfg.B * cfg.H * (2 * 40960 + 256 + 256 + 160 + 4 + 320)
 
 
+def test_read_launch_write_bytes():
+    """What a read launch writes: y (V fp32) and the appended token (k, v bf16,
+    decay and beta fp32) of every item; c1 24.2 MB, c3 (Gated DeltaNet, K = V =
+    128) 256 x 32 x (512 + 256 + 256 + 4 + 4) B."""
+    c1, c3 = CONFIGS["c1"], CONFIGS["c3"]
+    assert bench.read_write_bytes(c1) == 256 * 128 * (320 + 256 + 160 + 4)
+    assert bench.read_write_bytes(c3) == 256 * 32 * (512 + 256 + 256 + 4 + 4)
+
+
 @pytest.mark.timeout(300)
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
