@@ -202,6 +202,18 @@ STREAM_BYTES = 1 << 30
 MIX_READS_PER_WRITE = 8
 
 
+def matched_probe(nbytes: int, wbytes: int):
+    """The streaming-probe launch that stands for a kernel launch of nbytes, of
+    which wbytes written: (bytes read, reads per write).  The mix is the
+    nearest the probe offers (2, 4, 8 or 16 reads per write); the size is
+    rounded to whole 64 KB chunks (either unroll) and capped at one probe
+    source, since a 1 GiB launch already streams at the full rate."""
+    reads = nbytes - wbytes
+    m = min((2, 4, 8, 16), key=lambda x: abs(np.log2(x) - np.log2(max(reads, 1) / max(wbytes, 1))))
+    chunk = 16 * 4096
+    return min(STREAM_BYTES, max(chunk, int(round(reads / chunk)) * chunk)), m
+
+
 def stream_ceilings(torch, Bnd, timed, dev, launches=()) -> dict:
     """Best rate (read + written bytes per second) of the streaming probe for
     an 8:1 read:write mix, for reads alone and for a 1:1 copy, each the best
@@ -227,7 +239,7 @@ def stream_ceilings(torch, Bnd, timed, dev, launches=()) -> dict:
     def launch(write_bytes, unroll, blocks, nt, read_bytes=STREAM_BYTES):
         i = turn[0]
         turn[0] += 1
-        regions = STREAM_BYTES // read_bytes   # disjoint regions per source
+        regions = max(1, STREAM_BYTES // read_bytes)   # disjoint regions per source
         src = srcs[i % 2][(i // 2) % regions * (read_bytes // 4):]
         span = max(write_bytes, 4096 * max(blocks, 1))  # bytes this launch writes
         slot = i % max(1, pool.numel() * 4 // span)
@@ -247,11 +259,8 @@ def stream_ceilings(torch, Bnd, timed, dev, launches=()) -> dict:
     ro = best(0, [(4, 1024), (8, 1024), (8, 2048), (16, 1024), (16, 2048)])
     cp = best(STREAM_BYTES, [(4, 0), (8, 0), (8, 4096)])
     matched_us, matched_mix = [], []
-    chunk = 16 * 4096          # whole chunks for either unroll
     for nbytes, wbytes in launches:
-        reads = nbytes - wbytes
-        m = min((2, 4, 8, 16), key=lambda x: abs(np.log2(x) - np.log2(max(reads, 1) / max(wbytes, 1))))
-        rd = max(chunk, int(round(reads / chunk)) * chunk)
+        rd, m = matched_probe(nbytes, wbytes)
         shapes = [(16, 0)] + ([(8, 0)] if m <= 8 else [])
         r_best = best(rd // m, shapes, rd)
         matched_us.append(nbytes / (r_best[0] * 1e3))   # the launch's bytes at the probe's rate

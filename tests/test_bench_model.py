@@ -71,6 +71,25 @@ def test_read_launch_write_bytes():
     assert bench.read_write_bytes(c3) == 256 * 32 * (512 + 256 + 256 + 4 + 4)
 
 
+@pytest.mark.parametrize("name", ["c0", "c1", "c2", "c3", "c4"])
+def test_matched_probe_launches_fit_the_probe(name):
+    """The probe launches that stand for each window position's read: whole
+    64 KB chunks, a mix the probe accepts, and never more than one 1 GiB probe
+    source (c2's reads pass 1 GiB at high positions)."""
+    cfg = CONFIGS[name]
+    ranks = Workload(cfg).ranks
+    w = bench.read_write_bytes(cfg)
+    for p in range(cfg.W):
+        rd, m = bench.matched_probe(bench.read_bytes(cfg, ranks, p), w)
+        assert m in (2, 4, 8, 16)
+        assert 0 < rd <= bench.STREAM_BYTES and rd % (16 * 4096) == 0
+        assert rd % m == 0 and (rd // m) % 4096 == 0
+    # c1 at window position 0 reads 95 MB and writes 24 MB: about 4 reads per write
+    rd, m = bench.matched_probe(bench.read_bytes(CONFIGS["c1"], Workload(CONFIGS["c1"]).ranks, 0),
+                                bench.read_write_bytes(CONFIGS["c1"]))
+    assert m == 4 and abs(rd / 1e6 - 95.4) < 0.5
+
+
 @pytest.mark.timeout(300)
 def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
