@@ -1,11 +1,15 @@
 // SketchSSM decode read (sketch heads and dense-fallback heads) for gfx950.
 //
 // One launch serves one decode step of a layer; work items are (b, h) pairs.
-// Blocks follow the plan's head order: first one block per item of every dense
-// head (a dense item streams its whole fp32 state, ~21x the bytes of a rank-6
-// sketch item), then, per sketch head from high rank buckets to low, blocks of
-// 16 batch rows with one 16-lane DPP row per item.  Consecutive blocks land on
-// different XCDs, so the heavy dense items spread over the chip first.
+// Blocks follow the plan's order of the sketch heads, from high rank buckets to
+// low, each as blocks of 16 batch rows with one 16-lane DPP row per item; one
+// block per item of every dense head comes last.  A dense item streams its
+// whole fp32 state (~21x the bytes of a rank-6 sketch item), but its block moves
+// fewer bytes than a 16-row sketch block and ends sooner, and a launch usually
+// holds more waves than the chip keeps resident (9152 against 8192 for a
+// 128-head Nano-shaped layer at batch 256), so the
+// blocks that start late, when the first ones end, are best the shortest: the
+// longest-first order by block, not by item.
 //
 // Per item the read
 //   * appends the current token (k, v, decay, beta) to window slot `pos`;
@@ -54,7 +58,7 @@ struct ReadArgs {
     const int32_t* pos_seq;  // per-sequence window positions (continuous batching) or null
     int B, H, pos;
     int Hk, share;     // key/query heads; each serves `share` consecutive heads
-    int n_dense;       // dense heads lead the order
+    int n_dense;       // dense heads lead the head table (their blocks run last)
     int tiles;         // ceil(B / 16) blocks per sketch head
     int dense_blocks;  // n_dense * B
 };
@@ -547,11 +551,13 @@ __global__ __launch_bounds__(kReadThreads)
 __attribute__((amdgpu_waves_per_eu(ReadOccupancy<KIND, V, QT, SEQ>::value)))
 void read_kernel(ReadArgs A, HeadTable T) {
     extern __shared__ float4 lds4[];  // token staging + coefficient map (sketch) or reduction buffers (dense)
+    // sketch tiles first, the dense heads' items last
     const int blk = blockIdx.x;
-    if (blk < A.dense_blocks) {
-        dense_block<KIND, V, QT, SEQ>(A, T, blk, lds4);
+    const int sketch_blocks = int(gridDim.x) - A.dense_blocks;
+    if (blk < sketch_blocks) {
+        sketch_block<KIND, V, QT, SEQ>(A, T, blk, lds4);
     } else {
-        sketch_block<KIND, V, QT, SEQ>(A, T, blk - A.dense_blocks, lds4);
+        dense_block<KIND, V, QT, SEQ>(A, T, blk - sketch_blocks, lds4);
     }
 }
 
