@@ -438,6 +438,9 @@ struct DenseLds {
     static constexpr int V4 = V / 4;
     static constexpr int KG = kReadThreads / V4;
     static constexpr size_t bytes = size_t(kK + V) * 4 + size_t(KG) * V4 * 16;
+    // Mamba-2, lockstep: each row's window term (score, decay, value) after the
+    // token staging
+    static constexpr size_t spread_bytes = size_t(2 * 16 + 16 * V) * 4;
 };
 
 template <int KIND, int V, typename QT, bool SEQ>
@@ -476,9 +479,68 @@ __device__ __forceinline__ void dense_block(const ReadArgs& A, const HeadTable& 
         sreg[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (owner && kk < K) sreg[j] = ldnt_f4(reinterpret_cast<const float*>(S4 + kk * V4 + v4));
     }
-    if (tid < 16) {
-        using RS = RowSweep<KIND, V, QT, !SEQ>;
-        char* stg = reinterpret_cast<char*>(lds4) + DenseLds<V>::bytes;
+    using RS = RowSweep<KIND, V, QT, !SEQ>;
+    char* stg = reinterpret_cast<char*>(lds4) + DenseLds<V>::bytes;
+    if constexpr (M2 && !SEQ) {
+        // Mamba-2 decays are scalars, so the window's terms do not depend on
+        // one another: row j > 0 reads window slot pos - j and forms its k . q
+        // while row 0 reads the current token, all in one round trip; row 0
+        // then adds the terms in the row sweep's order (slot pos - 1 first, the
+        // same decay products), which gives the sweep's result bit for bit.
+        float* sc_s = reinterpret_cast<float*>(stg + RS::kStageBytes);  // [16] raw scores
+        float* a_s = sc_s + 16;                                          // [16] decays
+        float* v_s = a_s + 16;                                           // [16][V] values
+        const int row = tid >> 4, l = tid & 15;
+        const int kh = h / A.share;
+        const size_t itemk = size_t(b) * A.Hk + kh;
+        const bool vl = l < V / 8;
+        const int vo = vl ? 8 * l : 0;
+        // rows past the window's start re-read the current token (in bounds,
+        // unused), so the loads need no branch
+        const bool win = row > 0 && row <= pos;
+        const size_t i = size_t(win ? pos - row : 0);
+        const size_t kslot = (i * A.Hk + kh) * A.B + b;
+        const size_t slot = (i * A.H + h) * A.B + b;
+        const typename V8::raw_t qj = V8::load(A.q, itemk * kK + 8 * l);
+        const typename V8::raw_t kw = V8::load(win ? A.kbuf : A.k, (win ? kslot : itemk) * kK + 8 * l);
+        const typename V8::raw_t vw = V8::load(win ? A.vbuf : A.v, (win ? slot : item) * V + vo);
+        const float aw = (win ? A.abuf + slot : A.a + item)[0];
+        const float sj = row_sum16(raw_dot8<QT>(kw, qj));
+        float vf[8];
+        V8::unpack(vw, vf);
+        if (row == 0) {
+            V8::store(stg + RS::kStageK, 8 * l, kw);
+            if (vl) V8::store(stg + RS::kStageV, 8 * l, vw);
+            if (l == 0) reinterpret_cast<float*>(stg + RS::kStageS)[0] = aw;
+        } else if (win) {
+            if (vl) store8f(v_s + row * V + vo, vf);
+            if (l == 0) {
+                sc_s[row] = sj;
+                a_s[row] = aw;
+            }
+        }
+        __syncthreads();
+        if (row == 0) {
+            float acc[8], u[8], q[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = sj * vf[e];
+            float g = aw;
+            for (int j = 1; j <= pos; ++j) {
+                const float s = sc_s[j] * g;
+                float vv[8];
+                load8f(v_s + j * V + vo, vv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = fmaf(s, vv[e], acc[e]);
+                g *= a_s[j];
+            }
+            V8::unpack(qj, q);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) u[e] = g * q[e];
+            store8f(qt_s + 8 * l, u);
+            if (vl) store8f(intra_s + 8 * l, acc);
+            RS::append(A, b, h, l, pos, stg);
+        }
+    } else if (tid < 16) {
         typename V8::raw_t qr;
         float u[8], acc[8], g = 1.f;
         RS::run(A, b, h, tid, pos, qr, u, acc, g, stg);
@@ -534,12 +596,13 @@ __device__ __forceinline__ void dense_block(const ReadArgs& A, const HeadTable& 
 }
 
 // Waves per SIMD the register budget is sized for: 8 (64 VGPRs) where the
-// sweep fits, 5 (96 VGPRs) for the wider per-channel / fp32 variants, 4 (128)
-// for the fp32 V = 128 per-sequence instances, which need a little more.
+// sweep fits (Mamba-2 with bf16 tokens up to V = 112), 5 (96 VGPRs) for the
+// wider per-channel / fp32 variants, 4 (128) for the fp32 V = 128 per-sequence
+// instances, which need a little more.
 template <int KIND, int V, typename QT, bool SEQ>
 struct ReadOccupancy {
     static constexpr bool kF32 = std::is_same<QT, F32Tag>::value;
-    static constexpr int value = (KIND == SKSSM_MAMBA2 && V <= 80 && !kF32) ? 8
+    static constexpr int value = (KIND == SKSSM_MAMBA2 && V <= 112 && !kF32) ? 8
                                  : (SEQ && kF32 && V == 128)               ? 4
                                                                             : 5;
 };
@@ -651,12 +714,13 @@ static sketchssm_status run_read(const sketchssm_shape& sh, const HeadTable& t, 
     if (n_sketch > 0) lds = kRows * stage + size_t(map_rows) * kK * sizeof(float);
     if (n_dense > 0) {
         size_t dl = stage;
+        const bool spread = sh.kind == SKSSM_MAMBA2 && !pos_seq;  // the dense block's window terms
         switch (sh.V) {
-            case 64: dl += DenseLds<64>::bytes; break;
-            case 80: dl += DenseLds<80>::bytes; break;
-            case 96: dl += DenseLds<96>::bytes; break;
-            case 112: dl += DenseLds<112>::bytes; break;
-            default: dl += DenseLds<128>::bytes; break;
+            case 64: dl += DenseLds<64>::bytes + (spread ? DenseLds<64>::spread_bytes : 0); break;
+            case 80: dl += DenseLds<80>::bytes + (spread ? DenseLds<80>::spread_bytes : 0); break;
+            case 96: dl += DenseLds<96>::bytes + (spread ? DenseLds<96>::spread_bytes : 0); break;
+            case 112: dl += DenseLds<112>::bytes + (spread ? DenseLds<112>::spread_bytes : 0); break;
+            default: dl += DenseLds<128>::bytes + (spread ? DenseLds<128>::spread_bytes : 0); break;
         }
         lds = lds > dl ? lds : dl;
     }
