@@ -103,8 +103,11 @@ typedef struct sketchssm_plan sketchssm_plan;   /* opaque, immutable once made *
  * Frames are the distinct (group, rank) pairs of the sketch heads sorted by
  * group then rank; bucket[h] = 0 (dense) or 1 + (rank-1)/8; the order lists
  * dense heads first, then buckets from high to low, heads ascending within a
- * bucket.  Both arrays are copied; *out receives a plan to free with
- * sketchssm_plan_destroy.  A plan may be shared by threads and streams.
+ * bucket.  The decode read launches the sketch heads' tiles in that order and
+ * the dense heads' items after them (a dense item's block moves fewer bytes
+ * than a 16-row sketch tile's).  Both arrays are copied; *out receives a plan
+ * to free with sketchssm_plan_destroy.  A plan may be shared by threads and
+ * streams.
  */
 sketchssm_status sketchssm_plan_create(const sketchssm_shape* shape, const int32_t* rank,
                                        const int32_t* group, sketchssm_plan** out);
